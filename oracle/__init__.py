@@ -50,6 +50,8 @@ from .attention import (  # noqa: F401
     rope,
     attend_rows,
     Cache,
+    write_kv,
+    attend_tokens,
     prefill,
     decode,
     verify,

@@ -171,6 +171,65 @@ def _prologue_k(k, pos, theta, eps, k_w):
     return bf16_round(rope(rmsnorm(k, k_w, eps), pos, theta))
 
 
+def write_kv(cache: Cache, k, v, seq, pos, *, theta, eps, k_w=None):
+    """Cache writes of a call: K[seq[t], :, pos[t]] = bf16(k'), V = v.
+
+    k/v [T, Hkv, d].  Returns the new cache (the input is not modified).
+    """
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    seq = np.asarray(seq, dtype=np.int64)
+    pos = np.asarray(pos, dtype=np.int64)
+    cap = cache.k.shape[2]
+    if len(pos) and (pos.min() < 0 or pos.max() >= cap):
+        raise ValueError("position outside the cache")
+    c = cache.copy()
+    kp = _prologue_k(k, pos[:, None], theta, eps, k_w)  # [T, Hkv, d]
+    for t in range(len(pos)):
+        c.k[seq[t], :, pos[t]] = kp[t]
+        c.v[seq[t], :, pos[t]] = v[t]
+    return c
+
+
+def attend_tokens(cache: Cache, q, seq, pos, *, scale, theta, eps, q_w=None,
+                  rows=None):
+    """Attention of tokens over the cache: token t, head h sees slots
+    0..pos[t] of row seq[t], KV head h // G.
+
+    q [T, Hq, d].  ``rows`` optionally restricts the work to a list of
+    (t, h) pairs (the other outputs stay zero).  Returns out [T, Hq, d] and
+    lse [T, Hq].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    seq = np.asarray(seq, dtype=np.int64)
+    pos = np.asarray(pos, dtype=np.int64)
+    T, Hq, d = q.shape
+    Hkv = cache.k.shape[1]
+    if Hq % Hkv:
+        raise ValueError("n_q_heads must be a multiple of n_kv_heads")
+    G = Hq // Hkv
+    out = np.zeros((T, Hq, d))
+    lse = np.zeros((T, Hq))
+    if rows is None:
+        qp = rope(rmsnorm(q, q_w, eps), pos[:, None], theta)  # [T, Hq, d]
+        for b in np.unique(seq):
+            idx = np.nonzero(seq == b)[0]
+            for h in range(Hq):
+                o, l = attend_rows(qp[idx, h], cache.k[b, h // G],
+                                   cache.v[b, h // G], scale, pos[idx] + 1)
+                out[idx, h] = o
+                lse[idx, h] = l
+        return out, lse
+    for t, h in rows:
+        qp = rope(rmsnorm(q[t, h], q_w, eps), pos[t], theta)
+        b = seq[t]
+        o, l = attend_rows(qp[None], cache.k[b, h // G], cache.v[b, h // G],
+                           scale, [pos[t] + 1])
+        out[t, h] = o[0]
+        lse[t, h] = l[0]
+    return out, lse
+
+
 def _forward(cache: Cache, q, k, v, seq, pos, *, scale, theta, eps,
              q_w=None, k_w=None):
     """Shared body of prefill / decode / verify for a flat list of tokens.
@@ -181,37 +240,9 @@ def _forward(cache: Cache, q, k, v, seq, pos, *, scale, theta, eps,
     q [T, Hq, d], k/v [T, Hkv, d].  Returns (out [T, Hq, d], lse [T, Hq],
     new cache).
     """
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
-    seq = np.asarray(seq, dtype=np.int64)
-    pos = np.asarray(pos, dtype=np.int64)
-    T, Hq, d = q.shape
-    Hkv = k.shape[1]
-    if Hq % Hkv:
-        raise ValueError("n_q_heads must be a multiple of n_kv_heads")
-    G = Hq // Hkv
-    cap = cache.k.shape[2]
-    if T and (pos.min() < 0 or pos.max() >= cap):
-        raise ValueError("position outside the cache")
-    c = cache.copy()
-    # writes
-    kp = _prologue_k(k, pos[:, None], theta, eps, k_w)  # [T, Hkv, d]
-    for t in range(T):
-        c.k[seq[t], :, pos[t]] = kp[t]
-        c.v[seq[t], :, pos[t]] = v[t]
-    # attention
-    qp = rope(rmsnorm(q, q_w, eps), pos[:, None], theta)  # [T, Hq, d]
-    out = np.zeros((T, Hq, d))
-    lse = np.zeros((T, Hq))
-    for b in np.unique(seq):
-        rows = np.nonzero(seq == b)[0]
-        for h in range(Hq):
-            g = h // G
-            o, l = attend_rows(qp[rows, h], c.k[b, g], c.v[b, g], scale,
-                               pos[rows] + 1)
-            out[rows, h] = o
-            lse[rows, h] = l
+    c = write_kv(cache, k, v, seq, pos, theta=theta, eps=eps, k_w=k_w)
+    out, lse = attend_tokens(c, q, seq, pos, scale=scale, theta=theta,
+                             eps=eps, q_w=q_w)
     return out, lse, c
 
 
@@ -305,6 +336,7 @@ def argmax_lowest(logits) -> int:
 
 __all__ = [
     "bf16_round", "bf16_bits", "bits_to_f64", "rmsnorm", "rope_inv_freq",
-    "rope", "attend_rows", "Cache", "prefill", "decode", "verify",
+    "rope", "attend_rows", "Cache", "write_kv", "attend_tokens", "prefill",
+    "decode", "verify",
     "lm_logits", "margin_ok", "argmax_lowest",
 ]

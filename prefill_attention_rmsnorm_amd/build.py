@@ -1,0 +1,73 @@
+"""Build libqa.so (HIP, gfx950) in-tree with hipcc.
+
+Every source under ``csrc/`` is compiled to an object under ``_build/`` and
+linked into ``libqa.so`` next to this file.  Packed-FP32 instructions are
+disabled (``-packed-fp32-ops``) for all device code.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libqa.so")
+ARCH = "gfx950"
+
+SOURCES = ["qa_api.cpp", "util.hip", "prefill.hip", "decode.hip", "verify.hip"]
+HEADERS = ["qa_internal.h", "qa_device.h", "attn_tile.h"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc",
+                 shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm not installed?)")
+
+
+def _flags():
+    return [
+        f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
+        "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wno-unused-command-line-argument",
+    ]
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc()] + _flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n"
+                           f"{r.stderr}")
+    return obj
+
+
+def build(verbose: bool = True) -> str:
+    """Compile every source and link libqa.so; returns the library path."""
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = min(len(SOURCES), int(os.environ.get("MAX_JOBS", "8")))
+    with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] \
+        + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}", file=sys.stderr)
+    return LIB
+
+
+if __name__ == "__main__":
+    build()

@@ -1,0 +1,433 @@
+// Host side of libqa: argument validation, launch, counters, error text.
+//
+// pegainfer PR #862 (SM120 FlashInfer GDN prefill), review thread: the C ABI
+// around the kernels validates ABI and geometry and fails instead of silently
+// running another kernel, and counts successful launches so that tests can
+// prove which kernel ran.  Every check below runs before any HIP call.
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "qa.h"
+#include "qa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+std::atomic<uint64_t> g_counters[8];
+
+enum {
+  CNT_PREFILL = 0, CNT_DECODE, CNT_VERIFY, CNT_KERNELS, CNT_REJECTED,
+  CNT_HIP_FAIL, CNT_WS_INIT, CNT_COPY
+};
+
+qa_status fail(qa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  g_counters[CNT_REJECTED].fetch_add(1);
+  return s;
+}
+
+qa_status hip_fail(hipError_t e, const char* what) {
+  char buf[512];
+  snprintf(buf, sizeof buf, "%s: %s", what, hipGetErrorString(e));
+  g_last_error = buf;
+  g_counters[CNT_HIP_FAIL].fetch_add(1);
+  return QA_ERR_HIP;
+}
+
+bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool al4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+#define QA_REQUIRE(cond, status, ...) \
+  do {                                 \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+qa_status check_cache(const qa_cache* c) {
+  QA_REQUIRE(c, QA_ERR_NULL, "cache descriptor is NULL");
+  QA_REQUIRE(c->k && c->v, QA_ERR_NULL, "cache k/v memory is NULL");
+  QA_REQUIRE(c->head_dim == qa::kHeadDim, QA_ERR_UNSUPPORTED,
+             "head_dim %d unsupported (only 128)", c->head_dim);
+  QA_REQUIRE(c->batch >= 1 && c->n_kv_heads >= 1 && c->capacity >= 1,
+             QA_ERR_SHAPE, "cache batch/n_kv_heads/capacity must be >= 1");
+  QA_REQUIRE(al16(c->k) && al16(c->v), QA_ERR_ALIGN,
+             "cache k/v must be 16-byte aligned");
+  QA_REQUIRE(c->stride_pos >= qa::kHeadDim && c->stride_h >= 1 && c->stride_b >= 1,
+             QA_ERR_SHAPE, "cache strides too small");
+  QA_REQUIRE(c->stride_pos % 8 == 0 && c->stride_h % 8 == 0 && c->stride_b % 8 == 0,
+             QA_ERR_ALIGN, "cache strides must be multiples of 8 elements");
+  return QA_OK;
+}
+
+qa_status check_params(const qa_params* p, const qa_cache* c, int* group) {
+  QA_REQUIRE(p, QA_ERR_NULL, "params is NULL");
+  QA_REQUIRE(p->n_q_heads >= 1, QA_ERR_SHAPE, "n_q_heads must be >= 1");
+  QA_REQUIRE(p->n_q_heads % c->n_kv_heads == 0, QA_ERR_SHAPE,
+             "n_q_heads %d is not a multiple of n_kv_heads %d", p->n_q_heads,
+             c->n_kv_heads);
+  const int G = p->n_q_heads / c->n_kv_heads;
+  QA_REQUIRE(G == 1 || G == 2 || G == 4 || G == 8, QA_ERR_UNSUPPORTED,
+             "GQA group %d unsupported (1, 2, 4 or 8)", G);
+  QA_REQUIRE(std::isfinite(p->rope_theta) && p->rope_theta > 0.0, QA_ERR_SHAPE,
+             "rope_theta must be finite and > 0");
+  QA_REQUIRE(std::isfinite(p->rms_eps) && p->rms_eps >= 0.0, QA_ERR_SHAPE,
+             "rms_eps must be finite and >= 0");
+  QA_REQUIRE(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.f,
+             QA_ERR_SHAPE, "softmax_scale must be finite and > 0");
+  QA_REQUIRE(al16(p->q_norm_w) && al16(p->k_norm_w), QA_ERR_ALIGN,
+             "norm weights must be 16-byte aligned");
+  *group = G;
+  return QA_OK;
+}
+
+qa::RopeFreq make_freq(double theta) {
+  qa::RopeFreq f;
+  for (int i = 0; i < qa::kHalf; ++i)
+    f.inv_freq[i] = std::pow(theta, -(2.0 * i) / qa::kHeadDim);
+  return f;
+}
+
+qa::CacheArgs cache_args(const qa_cache* c) {
+  qa::CacheArgs a;
+  a.k = static_cast<uint16_t*>(c->k);
+  a.v = static_cast<uint16_t*>(c->v);
+  a.sb = c->stride_b;
+  a.sh = c->stride_h;
+  a.sp = c->stride_pos;
+  a.capacity = c->capacity;
+  return a;
+}
+
+int group_of(int n_q_heads, int n_kv_heads) {
+  if (n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads) return 0;
+  const int G = n_q_heads / n_kv_heads;
+  return (G == 1 || G == 2 || G == 4 || G == 8) ? G : 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+qa_status qa_cache_alloc(qa_cache* out, int batch, int n_kv_heads, int capacity,
+                         int head_dim, void* k_mem, void* v_mem) {
+  QA_REQUIRE(out, QA_ERR_NULL, "out is NULL");
+  QA_REQUIRE((k_mem == nullptr) == (v_mem == nullptr), QA_ERR_NULL,
+             "pass both k_mem and v_mem, or neither");
+  QA_REQUIRE(head_dim == qa::kHeadDim, QA_ERR_UNSUPPORTED,
+             "head_dim %d unsupported (only 128)", head_dim);
+  QA_REQUIRE(batch >= 1 && n_kv_heads >= 1 && capacity >= 1, QA_ERR_SHAPE,
+             "batch, n_kv_heads and capacity must be >= 1");
+  QA_REQUIRE(!k_mem || (al16(k_mem) && al16(v_mem)), QA_ERR_ALIGN,
+             "k_mem/v_mem must be 16-byte aligned");
+  qa_cache c;
+  std::memset(&c, 0, sizeof c);
+  c.batch = batch;
+  c.n_kv_heads = n_kv_heads;
+  c.capacity = capacity;
+  c.head_dim = head_dim;
+  c.stride_pos = head_dim;
+  c.stride_h = (int64_t)capacity * head_dim;
+  c.stride_b = (int64_t)n_kv_heads * c.stride_h;
+  if (k_mem) {
+    c.k = k_mem;
+    c.v = v_mem;
+    c.owns = 0;
+  } else {
+    const size_t bytes = (size_t)batch * c.stride_b * sizeof(uint16_t);
+    hipError_t e = hipMalloc(&c.k, bytes);
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc(cache k)");
+    e = hipMalloc(&c.v, bytes);
+    if (e != hipSuccess) {
+      (void)hipFree(c.k);
+      return hip_fail(e, "hipMalloc(cache v)");
+    }
+    c.owns = 1;
+  }
+  *out = c;
+  return QA_OK;
+}
+
+qa_status qa_cache_free(qa_cache* c) {
+  QA_REQUIRE(c, QA_ERR_NULL, "cache descriptor is NULL");
+  if (c->owns) {
+    hipError_t e1 = hipFree(c->k), e2 = hipFree(c->v);
+    std::memset(c, 0, sizeof *c);
+    if (e1 != hipSuccess) return hip_fail(e1, "hipFree(cache k)");
+    if (e2 != hipSuccess) return hip_fail(e2, "hipFree(cache v)");
+    return QA_OK;
+  }
+  std::memset(c, 0, sizeof *c);
+  return QA_OK;
+}
+
+size_t qa_workspace_bytes(int op, int batch, int n_q_heads, int n_kv_heads,
+                          int max_ctx, int block_len) {
+  const int G = group_of(n_q_heads, n_kv_heads);
+  if (!G || batch < 1 || max_ctx < 0) return 0;
+  switch (op) {
+    case QA_OP_PREFILL:
+      return qa::prefill_ws_bytes(max_ctx);
+    case QA_OP_DECODE:
+      if (max_ctx < 1) return 0;
+      return qa::split_layout(batch, n_kv_heads, G, max_ctx,
+                              qa::decode_keys_per_split(batch, n_kv_heads, max_ctx))
+          .total;
+    case QA_OP_VERIFY:
+      if (max_ctx < 1 || block_len < 1 || block_len * G > 128) return 0;
+      return qa::split_layout(batch, n_kv_heads, block_len * G, max_ctx,
+                              qa::verify_keys_per_split(batch, n_kv_heads, max_ctx))
+          .total;
+    default:
+      return 0;
+  }
+}
+
+qa_status qa_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  QA_REQUIRE(ws, QA_ERR_NULL, "workspace is NULL");
+  QA_REQUIRE(al16(ws), QA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  QA_REQUIRE(ws_bytes >= qa::kWsHeader && ws_bytes % 16 == 0, QA_ERR_WORKSPACE,
+             "workspace must be >= 256 bytes and a multiple of 16");
+  hipError_t e = qa::launch_fill_zero(ws, ws_bytes, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "workspace fill kernel");
+  g_counters[CNT_WS_INIT].fetch_add(1);
+  g_counters[CNT_KERNELS].fetch_add(1);
+  return QA_OK;
+}
+
+qa_status qa_prefill(const qa_cache* c, const qa_params* p, const void* q,
+                     const void* k, const void* v, int64_t q_tok_stride,
+                     int64_t kv_tok_stride, const int32_t* cu_seqlens,
+                     const int32_t* positions, int n_seq, int total_tokens,
+                     int max_seqlen, void* out, float* lse, void* ws,
+                     size_t ws_bytes, void* stream) {
+  qa_status st = check_cache(c);
+  if (st != QA_OK) return st;
+  int G = 0;
+  st = check_params(p, c, &G);
+  if (st != QA_OK) return st;
+  QA_REQUIRE(total_tokens >= 0, QA_ERR_SHAPE, "total_tokens must be >= 0");
+  if (total_tokens == 0) {
+    g_last_error.clear();
+    return QA_OK;
+  }
+  QA_REQUIRE(q && k && v && out && cu_seqlens && positions && ws, QA_ERR_NULL,
+             "q, k, v, out, cu_seqlens, positions and ws must be non-NULL");
+  QA_REQUIRE(n_seq >= 1 && n_seq <= c->batch, QA_ERR_SHAPE,
+             "n_seq %d must be in [1, cache batch %d]", n_seq, c->batch);
+  QA_REQUIRE(max_seqlen >= 1, QA_ERR_SHAPE, "max_seqlen must be >= 1");
+  QA_REQUIRE(max_seqlen <= c->capacity, QA_ERR_CAPACITY,
+             "max_seqlen %d exceeds cache capacity %d", max_seqlen, c->capacity);
+  QA_REQUIRE(q_tok_stride >= (int64_t)p->n_q_heads * qa::kHeadDim &&
+                 kv_tok_stride >= (int64_t)c->n_kv_heads * qa::kHeadDim,
+             QA_ERR_SHAPE, "token strides smaller than one token's heads");
+  QA_REQUIRE(q_tok_stride % 8 == 0 && kv_tok_stride % 8 == 0, QA_ERR_ALIGN,
+             "token strides must be multiples of 8 elements");
+  QA_REQUIRE(al16(q) && al16(k) && al16(v) && al16(out) && al16(ws) && al4(lse) &&
+                 al4(cu_seqlens) && al4(positions),
+             QA_ERR_ALIGN, "q/k/v/out/ws must be 16-byte aligned");
+  QA_REQUIRE(ws_bytes >= qa::prefill_ws_bytes(total_tokens), QA_ERR_WORKSPACE,
+             "workspace %zu bytes < %zu needed", ws_bytes,
+             qa::prefill_ws_bytes(total_tokens));
+  QA_REQUIRE((long long)n_seq * c->n_kv_heads * ((max_seqlen + 127) / 128) * 8 < (1LL << 31),
+             QA_ERR_SHAPE, "launch grid too large");
+
+  qa::PrefillArgs a;
+  a.c = cache_args(c);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.q_tok_stride = q_tok_stride;
+  a.kv_tok_stride = kv_tok_stride;
+  a.cu_seqlens = cu_seqlens;
+  a.positions = positions;
+  a.n_seq = n_seq;
+  a.total_tokens = total_tokens;
+  a.max_seqlen = max_seqlen;
+  a.n_qtiles = 0;
+  a.n_q_heads = p->n_q_heads;
+  a.n_kv_heads = c->n_kv_heads;
+  a.q_norm_w = static_cast<const uint16_t*>(p->q_norm_w);
+  a.k_norm_w = static_cast<const uint16_t*>(p->k_norm_w);
+  a.eps = p->rms_eps;
+  a.qscale = (float)((double)p->softmax_scale * 1.4426950408889634);
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.err = static_cast<int*>(ws);
+  a.cs = reinterpret_cast<float2*>(static_cast<char*>(ws) + qa::kWsHeader);
+  int nk = 0;
+  hipError_t e = qa::launch_prefill(a, make_freq(p->rope_theta), G,
+                                    static_cast<hipStream_t>(stream), &nk);
+  g_counters[CNT_KERNELS].fetch_add(nk);
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  g_counters[CNT_PREFILL].fetch_add(1);
+  g_last_error.clear();
+  return QA_OK;
+}
+
+static qa_status fill_split_args(qa::DecodeArgs& a, const qa_cache* c,
+                                 const qa_params* p, const void* q,
+                                 const void* k, const void* v,
+                                 const int32_t* pos, int batch, int block_len,
+                                 int max_ctx, void* out, float* lse, void* ws,
+                                 const qa::SplitLayout& L) {
+  a.c = cache_args(c);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.positions = pos;
+  a.batch = batch;
+  a.block_len = block_len;
+  a.max_ctx = max_ctx;
+  a.n_q_heads = p->n_q_heads;
+  a.n_kv_heads = c->n_kv_heads;
+  a.keys_per_split = L.keys_per_split;
+  a.n_split = L.n_split;
+  a.q_norm_w = static_cast<const uint16_t*>(p->q_norm_w);
+  a.k_norm_w = static_cast<const uint16_t*>(p->k_norm_w);
+  a.eps = p->rms_eps;
+  a.qscale = (float)((double)p->softmax_scale * 1.4426950408889634);
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  char* base = static_cast<char*>(ws);
+  a.err = reinterpret_cast<int*>(base);
+  a.counters = reinterpret_cast<int*>(base + L.counters_off);
+  a.part_m = reinterpret_cast<float*>(base + L.m_off);
+  a.part_l = reinterpret_cast<float*>(base + L.l_off);
+  a.part_o = reinterpret_cast<float*>(base + L.o_off);
+  return QA_OK;
+}
+
+qa_status qa_decode(const qa_cache* c, const qa_params* p, const void* q,
+                    const void* k, const void* v, const int32_t* positions,
+                    int batch, int max_ctx, void* out, float* lse, void* ws,
+                    size_t ws_bytes, void* stream) {
+  qa_status st = check_cache(c);
+  if (st != QA_OK) return st;
+  int G = 0;
+  st = check_params(p, c, &G);
+  if (st != QA_OK) return st;
+  QA_REQUIRE(q && k && v && out && positions && ws, QA_ERR_NULL,
+             "q, k, v, out, positions and ws must be non-NULL");
+  QA_REQUIRE(batch >= 1 && batch <= c->batch, QA_ERR_SHAPE,
+             "batch %d must be in [1, cache batch %d]", batch, c->batch);
+  QA_REQUIRE(max_ctx >= 1, QA_ERR_SHAPE, "max_ctx must be >= 1");
+  QA_REQUIRE(max_ctx <= c->capacity, QA_ERR_CAPACITY,
+             "max_ctx %d exceeds cache capacity %d", max_ctx, c->capacity);
+  QA_REQUIRE(al16(q) && al16(k) && al16(v) && al16(out) && al16(ws) && al4(lse) &&
+                 al4(positions),
+             QA_ERR_ALIGN, "q/k/v/out/ws must be 16-byte aligned");
+  const qa::SplitLayout L = qa::split_layout(
+      batch, c->n_kv_heads, G, max_ctx,
+      qa::decode_keys_per_split(batch, c->n_kv_heads, max_ctx));
+  QA_REQUIRE(ws_bytes >= L.total, QA_ERR_WORKSPACE,
+             "workspace %zu bytes < %zu needed", ws_bytes, L.total);
+  qa::DecodeArgs a;
+  fill_split_args(a, c, p, q, k, v, positions, batch, 1, max_ctx, out, lse, ws, L);
+  int nk = 0;
+  hipError_t e = qa::launch_decode(a, make_freq(p->rope_theta), G,
+                                   static_cast<hipStream_t>(stream), &nk);
+  g_counters[CNT_KERNELS].fetch_add(nk);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  g_counters[CNT_DECODE].fetch_add(1);
+  g_last_error.clear();
+  return QA_OK;
+}
+
+qa_status qa_verify(const qa_cache* c, const qa_params* p, const void* q,
+                    const void* k, const void* v, const int32_t* start_pos,
+                    int batch, int block_len, int max_ctx, void* out,
+                    float* lse, void* ws, size_t ws_bytes, void* stream) {
+  qa_status st = check_cache(c);
+  if (st != QA_OK) return st;
+  int G = 0;
+  st = check_params(p, c, &G);
+  if (st != QA_OK) return st;
+  QA_REQUIRE(q && k && v && out && start_pos && ws, QA_ERR_NULL,
+             "q, k, v, out, start_pos and ws must be non-NULL");
+  QA_REQUIRE(batch >= 1 && batch <= c->batch, QA_ERR_SHAPE,
+             "batch %d must be in [1, cache batch %d]", batch, c->batch);
+  QA_REQUIRE(block_len >= 1 && block_len * G <= 128, QA_ERR_SHAPE,
+             "block_len %d: need 1 <= block_len and block_len*G <= 128", block_len);
+  QA_REQUIRE(max_ctx >= block_len, QA_ERR_SHAPE, "max_ctx must be >= block_len");
+  QA_REQUIRE(max_ctx <= c->capacity, QA_ERR_CAPACITY,
+             "max_ctx %d exceeds cache capacity %d", max_ctx, c->capacity);
+  QA_REQUIRE(al16(q) && al16(k) && al16(v) && al16(out) && al16(ws) && al4(lse) &&
+                 al4(start_pos),
+             QA_ERR_ALIGN, "q/k/v/out/ws must be 16-byte aligned");
+  const qa::SplitLayout L = qa::split_layout(
+      batch, c->n_kv_heads, block_len * G, max_ctx,
+      qa::verify_keys_per_split(batch, c->n_kv_heads, max_ctx));
+  QA_REQUIRE(ws_bytes >= L.total, QA_ERR_WORKSPACE,
+             "workspace %zu bytes < %zu needed", ws_bytes, L.total);
+  qa::DecodeArgs a;
+  fill_split_args(a, c, p, q, k, v, start_pos, batch, block_len, max_ctx, out, lse,
+                  ws, L);
+  int nk = 0;
+  hipError_t e = qa::launch_verify(a, make_freq(p->rope_theta), G,
+                                   static_cast<hipStream_t>(stream), &nk);
+  g_counters[CNT_KERNELS].fetch_add(nk);
+  if (e != hipSuccess) return hip_fail(e, "verify launch");
+  g_counters[CNT_VERIFY].fetch_add(1);
+  g_last_error.clear();
+  return QA_OK;
+}
+
+qa_status qa_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  QA_REQUIRE(src && dst, QA_ERR_NULL, "src/dst NULL");
+  QA_REQUIRE(al16(src) && al16(dst) && bytes % 16 == 0, QA_ERR_ALIGN,
+             "copy needs 16-byte aligned pointers and size");
+  hipError_t e = qa::launch_copy(src, dst, bytes, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "copy launch");
+  g_counters[CNT_COPY].fetch_add(1);
+  g_counters[CNT_KERNELS].fetch_add(1);
+  return QA_OK;
+}
+
+const char* qa_status_str(qa_status s) {
+  switch (s) {
+    case QA_OK: return "QA_OK";
+    case QA_ERR_NULL: return "QA_ERR_NULL";
+    case QA_ERR_SHAPE: return "QA_ERR_SHAPE";
+    case QA_ERR_UNSUPPORTED: return "QA_ERR_UNSUPPORTED";
+    case QA_ERR_ALIGN: return "QA_ERR_ALIGN";
+    case QA_ERR_CAPACITY: return "QA_ERR_CAPACITY";
+    case QA_ERR_WORKSPACE: return "QA_ERR_WORKSPACE";
+    case QA_ERR_HIP: return "QA_ERR_HIP";
+  }
+  return "QA_ERR_UNKNOWN";
+}
+
+const char* qa_last_error(void) { return g_last_error.c_str(); }
+
+void qa_get_counters(uint64_t out[8]) {
+  for (int i = 0; i < 8; ++i) out[i] = g_counters[i].load();
+}
+
+void qa_reset_counters(void) {
+  for (int i = 0; i < 8; ++i) g_counters[i].store(0);
+}
+
+qa_status qa_device_error(void* ws, void* stream, int32_t* code) {
+  QA_REQUIRE(ws && code, QA_ERR_NULL, "ws/code NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  int32_t v = 0;
+  e = hipMemcpy(&v, ws, sizeof v, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "read error word");
+  const int32_t zero = 0;
+  e = hipMemcpy(ws, &zero, sizeof zero, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(e, "clear error word");
+  *code = v;
+  return QA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,136 @@
+// Internal declarations shared by the host library and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qa {
+
+constexpr int kHeadDim = 128;
+constexpr int kHalf = 64;        // rotation pairs per head
+constexpr int kKeyTile = 64;     // keys per LDS tile in the MFMA kernels
+constexpr size_t kWsHeader = 256;  // error word + reserved
+
+// Rotation frequencies theta^(-2i/128), computed on the host in fp64 and
+// passed by value (kernel arguments), so every kernel uses the same values.
+struct RopeFreq {
+  double inv_freq[kHalf];
+};
+
+// ---- workspace layout --------------------------------------------------------
+//   [0, 256)                 int32 error word at 0
+//   prefill: + cos/sin table float2 [total_tokens][64]
+//   decode / verify: + int32 merge counters [batch*n_kv_heads] (256-B rounded)
+//                    + fp32 m, l [batch][n_kv][n_split][rows] each
+//                    + fp32 o   [batch][n_kv][n_split][rows][128]
+// rows = G (decode) or block_len*G (verify).
+inline size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct SplitLayout {
+  int keys_per_split;
+  int n_split;
+  size_t counters_off, m_off, l_off, o_off, total;
+};
+
+// Decode: keys per split-K block.  Small grids use short splits so more
+// workgroups stream the cache; the count is a function of the launch sizes
+// only (never of device-side positions), so graphs stay valid.
+inline int decode_keys_per_split(int batch, int n_kv, int max_ctx) {
+  long pairs = (long)batch * n_kv;
+  int ks = 64;
+  // grow the split while the grid would still exceed ~2 workgroups per CU
+  while (ks < 128 && pairs * ((max_ctx + 2 * ks - 1) / (2 * ks)) >= 512) ks *= 2;
+  return ks;
+}
+
+// Verify: about one workgroup per CU in total; splits are whole 64-key tiles.
+inline int verify_keys_per_split(int batch, int n_kv, int max_ctx) {
+  long pairs = (long)batch * n_kv;
+  long want = pairs >= 256 ? 1 : 256 / pairs;  // splits per (sequence, kv head)
+  long ks = (max_ctx + want - 1) / want;
+  ks = (ks + kKeyTile - 1) / kKeyTile * kKeyTile;
+  return ks < kKeyTile ? kKeyTile : (int)ks;
+}
+
+inline SplitLayout split_layout(int batch, int n_kv, int rows, int max_ctx,
+                                int keys_per_split) {
+  SplitLayout L;
+  L.keys_per_split = keys_per_split;
+  L.n_split = (max_ctx + keys_per_split - 1) / keys_per_split;
+  if (L.n_split < 1) L.n_split = 1;
+  size_t pairs = (size_t)batch * n_kv;
+  size_t nrow = pairs * L.n_split * rows;
+  L.counters_off = kWsHeader;
+  L.m_off = L.counters_off + round256(pairs * sizeof(int));
+  L.l_off = L.m_off + round256(nrow * sizeof(float));
+  L.o_off = L.l_off + round256(nrow * sizeof(float));
+  L.total = L.o_off + round256(nrow * kHeadDim * sizeof(float));
+  return L;
+}
+
+inline size_t prefill_ws_bytes(int total_tokens) {
+  return kWsHeader + round256((size_t)total_tokens * kHalf * 2 * sizeof(float));
+}
+
+// ---- kernel argument blocks ----------------------------------------------------
+struct CacheArgs {
+  uint16_t* k;
+  uint16_t* v;
+  int64_t sb, sh, sp;  // element strides
+  int capacity;
+};
+
+struct PrefillArgs {
+  CacheArgs c;
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t q_tok_stride, kv_tok_stride;
+  const int32_t* cu_seqlens;
+  const int32_t* positions;
+  int n_seq, total_tokens, max_seqlen, n_qtiles;
+  int n_q_heads, n_kv_heads;
+  const uint16_t* q_norm_w;
+  const uint16_t* k_norm_w;
+  double eps;
+  float qscale;  // softmax_scale * log2(e), folded into q'
+  uint16_t* out;
+  float* lse;
+  int* err;
+  float2* cs;  // cos/sin table in the workspace
+};
+
+struct DecodeArgs {
+  CacheArgs c;
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* positions;  // decode: position per sequence; verify: start
+  int batch, block_len, max_ctx;
+  int n_q_heads, n_kv_heads;
+  int keys_per_split, n_split;
+  const uint16_t* q_norm_w;
+  const uint16_t* k_norm_w;
+  double eps;
+  float qscale;
+  uint16_t* out;
+  float* lse;
+  int* err;
+  int* counters;
+  float* part_m;
+  float* part_l;
+  float* part_o;
+};
+
+// ---- launchers (return the hipError_t of the launch) ------------------------------
+hipError_t launch_prefill(const PrefillArgs& a, const RopeFreq& f, int group,
+                          hipStream_t s, int* n_kernels);
+hipError_t launch_decode(const DecodeArgs& a, const RopeFreq& f, int group,
+                         hipStream_t s, int* n_kernels);
+hipError_t launch_verify(const DecodeArgs& a, const RopeFreq& f, int group,
+                         hipStream_t s, int* n_kernels);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+
+}  // namespace qa

@@ -1,0 +1,208 @@
+// Verification of a speculative draft block on gfx950.
+//
+// "dryft-flash-infer" agent guide, Where the wins are: speculative decoding
+// with exact verification reproduces the greedy argmax, so the block's rows
+// must equal what sequential decode steps would give.  The draft's
+// block_len tokens x G heads of one KV head form up to 128 query rows that
+// share every K/V tile (MFMA tile machinery of the prefill kernel); the keys
+// are split across workgroups, and the last workgroup of each
+// (sequence, kv head) merges the partials in split order.
+//
+// The workgroup whose key range holds some of the new slots first runs the
+// prologue for them (k' in fp64 with one RNE) and writes them to the cache;
+// only that workgroup ever reads those slots in this call, and the block
+// barrier orders its own writes before its reads.
+#include "attn_tile.h"
+#include "qa.h"
+
+namespace qa {
+
+template <int G, int NW>
+__global__ __launch_bounds__(NW * 64) void verify_kernel(DecodeArgs a, RopeFreq f) {
+  constexpr int NT = NW * 64;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStageBytes];
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int j = l & 31, h2 = l >> 5;
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int n = a.block_len, KS = a.keys_per_split;
+  const int rows = n * G;
+  const int L0 = a.positions[b];
+  const bool ok = L0 >= 0 && L0 + n <= a.max_ctx;
+  if (!ok && split == 0 && g == 0 && tid == 0) flag_error(a.err, QA_DEVERR_POSITION);
+  const int kv_end = ok ? L0 + n : 0;
+  const int k0 = split * KS, k1 = min(k0 + KS, kv_end);
+  const size_t pairidx = (size_t)b * a.n_kv_heads + g;
+  const size_t rowbase = (pairidx * a.n_split + split) * rows;
+
+  const int r = 32 * w + j;
+  const bool row_ok = r < rows;
+  const int hl = row_ok ? r / n : 0, ti = row_ok ? r % n : 0;
+  const int h = g * G + hl;
+  const int p = L0 + ti;
+
+  if (k0 < k1) {
+    // ---- new slots owned by this split: k' (fp64) and v into the cache
+    const int nb0 = max(k0, L0), nb1 = min(k1, L0 + n);
+    const double wk0 = a.k_norm_w ? (double)bf_to_f(a.k_norm_w[l]) : 1.0;
+    const double wk1 = a.k_norm_w ? (double)bf_to_f(a.k_norm_w[l + 64]) : 1.0;
+    for (int slot = nb0 + w; slot < nb1; slot += NW) {
+      const int i = slot - L0;
+      double sn, cn;
+      sincos((double)slot * f.inv_freq[l], &sn, &cn);
+      const size_t src = (((size_t)b * n + i) * a.n_kv_heads + g) * kHeadDim;
+      uint16_t o0, o1;
+      kprime_pair(a.k[src + l], a.k[src + l + 64], wk0, wk1, a.eps, cn, sn, &o0, &o1);
+      const size_t crow = (size_t)b * a.c.sb + (size_t)g * a.c.sh + (size_t)slot * a.c.sp;
+      a.c.k[crow + l] = o0;
+      a.c.k[crow + l + 64] = o1;
+      reinterpret_cast<uint32_t*>(a.c.v + crow)[l] =
+          reinterpret_cast<const uint32_t*>(a.v + src)[l];
+    }
+
+    // ---- cos/sin of the draft positions for the queries (LDS, fp64
+    // rotation recurrence from the block start, stored as fp32)
+    float2* cs = reinterpret_cast<float2*>(smem);  // [n][64], before staging
+    if (w == 0) {
+      double sb, cb, s1, c1;
+      sincos((double)L0 * f.inv_freq[l], &sb, &cb);
+      sincos(f.inv_freq[l], &s1, &c1);
+      for (int i = 0; i < n; ++i) {
+        cs[i * kHalf + l] = make_float2((float)cb, (float)sb);
+        const double cn = cb * c1 - sb * s1;
+        const double sn = sb * c1 + cb * s1;
+        cb = cn;
+        sb = sn;
+      }
+    }
+    __syncthreads();
+    u32x4 qb[8];
+    q_prologue(a.q + (((size_t)b * n + ti) * a.n_q_heads + h) * kHeadDim,
+               row_ok && ok, cs + ti * kHalf, a.q_norm_w, (float)a.eps,
+               a.qscale, h2, qb);
+    __syncthreads();  // cs and the new slots' cache writes are done
+
+    const uint16_t* kbase = a.c.k + (size_t)b * a.c.sb + (size_t)g * a.c.sh;
+    const uint16_t* vbase = a.c.v + (size_t)b * a.c.sb + (size_t)g * a.c.sh;
+    const int n_kt = (k1 - k0 + kKeyTile - 1) / kKeyTile;
+    WaveAttn st;
+    st.init();
+    TileStage<NT> stage;
+    stage.load(kbase, vbase, a.c.sp, k0, k1, 0, 0, nullptr, nullptr, tid);
+    stage.store(smem, tid);
+    __syncthreads();
+    for (int kt = 0; kt < n_kt; ++kt) {
+      const int kv0 = k0 + kt * kKeyTile;
+      if (kt + 1 < n_kt)
+        stage.load(kbase, vbase, a.c.sp, kv0 + kKeyTile, k1, 0, 0, nullptr,
+                   nullptr, tid);
+      const bool need_mask = (kv0 + kKeyTile > k1) || (kv0 + kKeyTile - 1 > L0);
+      st.tile(smem + (kt & 1) * kStageBytes, qb, kv0, need_mask,
+              row_ok ? p : -1, k1, j, h2);
+      if (kt + 1 < n_kt) stage.store(smem + ((kt + 1) & 1) * kStageBytes, tid);
+      __syncthreads();
+    }
+    if (row_ok) {
+      const float lt = st.lsum + __shfl_xor(st.lsum, 32);
+      if (h2 == 0) {
+        a.part_m[rowbase + r] = st.m;
+        a.part_l[rowbase + r] = lt;
+      }
+      float* po = a.part_o + (rowbase + r) * kHeadDim;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          float4 v4 = make_float4(st.o[db][4 * a4], st.o[db][4 * a4 + 1],
+                                  st.o[db][4 * a4 + 2], st.o[db][4 * a4 + 3]);
+          *reinterpret_cast<float4*>(po + 32 * db + 8 * a4 + 4 * h2) = v4;
+        }
+    }
+  } else {
+    for (int rr = tid; rr < rows; rr += NT) {
+      a.part_m[rowbase + rr] = -__builtin_inff();
+      a.part_l[rowbase + rr] = 0.f;
+    }
+  }
+
+  // ---- the last workgroup of this (sequence, kv head) merges the splits
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const int prev = __hip_atomic_fetch_add(a.counters + pairidx, 1, __ATOMIC_ACQ_REL,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (prev == a.n_split - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+
+  const size_t pbase = pairidx * a.n_split * rows;
+  for (int idx = tid; idx < rows * (kHeadDim / 4); idx += NT) {
+    const int rr = idx / (kHeadDim / 4), d4 = (idx % (kHeadDim / 4)) * 4;
+    float Mx = -__builtin_inff();
+    for (int s = 0; s < a.n_split; ++s) Mx = fmaxf(Mx, a.part_m[pbase + s * rows + rr]);
+    float L = 0.f;
+    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (Mx != -__builtin_inff()) {
+      for (int s = 0; s < a.n_split; ++s) {
+        const float ms = a.part_m[pbase + s * rows + rr];
+        if (ms == -__builtin_inff()) continue;
+        const float wgt = __builtin_amdgcn_exp2f(ms - Mx);
+        L += wgt * a.part_l[pbase + s * rows + rr];
+        const float4 po = *reinterpret_cast<const float4*>(
+            a.part_o + (pbase + s * rows + rr) * kHeadDim + d4);
+        O.x += wgt * po.x; O.y += wgt * po.y; O.z += wgt * po.z; O.w += wgt * po.w;
+      }
+    }
+    const bool good = ok && L > 0.f;
+    const float inv = good ? 1.0f / L : 0.f;
+    const int rhl = rr / n, rti = rr % n;
+    const size_t orow = (((size_t)b * n + rti) * a.n_q_heads + g * G + rhl) * kHeadDim;
+    u32x2 pr = {0u, 0u};
+    if (good) {
+      pr[0] = pack_bf16x2(O.x * inv, O.y * inv);
+      pr[1] = pack_bf16x2(O.z * inv, O.w * inv);
+    }
+    *reinterpret_cast<u32x2*>(a.out + orow + d4) = pr;
+    if (a.lse && d4 == 0)
+      a.lse[((size_t)b * n + rti) * a.n_q_heads + g * G + rhl] =
+          good ? (Mx + __log2f(L)) * kLn2 : 0.f;
+  }
+  if (tid == 0)
+    __hip_atomic_store(a.counters + pairidx, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int G>
+static hipError_t launch_verify_g(const DecodeArgs& a, const RopeFreq& f,
+                                  hipStream_t s) {
+  const dim3 grid(a.n_split, a.n_kv_heads, a.batch);
+  const int rows = a.block_len * G;
+  if (rows <= 32)
+    hipLaunchKernelGGL((verify_kernel<G, 1>), grid, dim3(64), 0, s, a, f);
+  else if (rows <= 64)
+    hipLaunchKernelGGL((verify_kernel<G, 2>), grid, dim3(128), 0, s, a, f);
+  else if (rows <= 128)
+    hipLaunchKernelGGL((verify_kernel<G, 4>), grid, dim3(256), 0, s, a, f);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_verify(const DecodeArgs& a, const RopeFreq& f, int group,
+                         hipStream_t s, int* n_kernels) {
+  *n_kernels = 0;
+  hipError_t e;
+  switch (group) {
+    case 1: e = launch_verify_g<1>(a, f, s); break;
+    case 2: e = launch_verify_g<2>(a, f, s); break;
+    case 4: e = launch_verify_g<4>(a, f, s); break;
+    case 8: e = launch_verify_g<8>(a, f, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e == hipSuccess) *n_kernels = 1;
+  return e;
+}
+
+}  // namespace qa

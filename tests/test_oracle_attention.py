@@ -320,3 +320,19 @@ def test_lse_merge_of_a_partition_equals_whole():
     om = (wA[:, None] * oA + wB[:, None] * oB) / (wA + wB)[:, None]
     assert np.allclose(om, o, atol=1e-14)
     assert np.allclose(np.logaddexp(lA, lB), l, atol=1e-14)
+
+
+def test_row_sampling_matches_full():
+    g = np.random.default_rng(15)
+    q, k, v, cu, pos = _rand_prefill(g, [6, 9], 4, 2, 16, 10)
+    seq = np.repeat([0, 1], [6, 9])
+    c = oracle.write_kv(oracle.Cache.empty(2, 2, 10, 16), k, v, seq, pos,
+                        theta=THETA, eps=EPS)
+    full, lf = oracle.attend_tokens(c, q, seq, pos, scale=0.25, theta=THETA,
+                                    eps=EPS)
+    rows = [(0, 0), (5, 3), (6, 1), (14, 2)]
+    part, lp = oracle.attend_tokens(c, q, seq, pos, scale=0.25, theta=THETA,
+                                    eps=EPS, rows=rows)
+    for t, h in rows:
+        assert np.allclose(part[t, h], full[t, h], atol=1e-14)
+        assert abs(lp[t, h] - lf[t, h]) < 1e-13
