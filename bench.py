@@ -1,0 +1,378 @@
+"""Benchmark of the GQA attention path on one MI355X.
+
+Workload: Qwen3-4B attention shapes, batch 4, 36 layers, 2048-token prompts,
+then 128 decode steps that each read all 36 layers' caches
+(4 x 8 x 2176 x 128 bf16 for K and for V per layer), plus one verification
+call of a 16-token draft block per sequence after a 2048-slot cache.
+
+One bench step = the whole path once:
+  prefill of all 36 layers (K/V prologue + flash attention per layer),
+  128 decode steps x 36 layers (each decode step is one captured HIP graph of
+  36 qa_decode launches plus the on-device position increment),
+  one qa_verify call (16-token block, batch 4, 2048 + 16 keys).
+Inputs are synthetic (seeded device draws, bf16 ~N(0,1)) and resident in HBM
+before timing starts.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GQA attn: decode µs/step + HBM GB/s; prefill TFLOP/s (B=4, ctx 2048)"
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 (256 CU x 2.4 GHz x 4096)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_info():
+    p = os.path.join(ROOT, "prefill_attention_rmsnorm_amd", "_build",
+                     "BUILD_INFO.json")
+    try:
+        with open(p) as f:
+            return json.load(f)
+    except OSError:
+        return {}
+
+
+class Workload:
+    """Device buffers of the benchmark workload."""
+
+    def __init__(self, torch, qa, W):
+        self.torch, self.qa = torch, qa
+        w = W.get(2)
+        self.w = w
+        self.B, self.L = w.batch, w.n_layers
+        self.Hq, self.Hkv, self.S = w.n_q_heads, w.n_kv_heads, w.prompt_lens[0]
+        self.cap, self.steps = w.capacity, w.decode_steps
+        dev = "cuda"
+        g = torch.Generator(device=dev)
+        g.manual_seed(2)
+        T = self.B * self.S
+
+        def rnd(*shape):
+            return torch.randn(*shape, generator=g, device=dev,
+                               dtype=torch.float32).to(torch.bfloat16)
+
+        log(f"bench: allocating {self.L} layers (caches + prefill inputs)")
+        self.caches = [qa.Cache.empty(self.B, self.Hkv, self.cap)
+                       for _ in range(self.L)]
+        self.pq = [rnd(T, self.Hq, 128) for _ in range(self.L)]
+        self.pk = [rnd(T, self.Hkv, 128) for _ in range(self.L)]
+        self.pv = [rnd(T, self.Hkv, 128) for _ in range(self.L)]
+        self.dq = [rnd(self.B, self.Hq, 128) for _ in range(self.L)]
+        self.dk = [rnd(self.B, self.Hkv, 128) for _ in range(self.L)]
+        self.dv = [rnd(self.B, self.Hkv, 128) for _ in range(self.L)]
+        self.params = qa.Params(self.Hq, w.scale, w.theta, w.eps)
+        cu = torch.arange(0, T + 1, self.S, dtype=torch.int32, device=dev)
+        self.cu = cu
+        self.ppos = torch.arange(self.S, dtype=torch.int32,
+                                 device=dev).repeat(self.B)
+        self.pout = torch.empty((T, self.Hq, 128), dtype=torch.bfloat16,
+                                device=dev)
+        self.pws = qa.workspace(qa.QA_OP_PREFILL, self.B, self.Hq, self.Hkv, T)
+        self.dpos = torch.full((self.B,), self.S, dtype=torch.int32,
+                               device=dev)
+        self.dpos0 = self.dpos.clone()
+        self.dout = torch.empty((self.B, self.Hq, 128), dtype=torch.bfloat16,
+                                device=dev)
+        self.dws = qa.workspace(qa.QA_OP_DECODE, self.B, self.Hq, self.Hkv,
+                                self.cap)
+        # verification workload: 2048 seeded slots + a 16-token block
+        w4 = W.get(4)
+        self.vB, self.vn, self.vL0, self.vcap = (w4.batch, w4.verify_block,
+                                                 w4.verify_start, w4.capacity)
+        self.vcache = qa.Cache.empty(self.vB, self.Hkv, self.vcap)
+        self.vcache.k[:, :, :self.vL0] = rnd(self.vB, self.Hkv, self.vL0, 128)
+        self.vcache.v[:, :, :self.vL0] = rnd(self.vB, self.Hkv, self.vL0, 128)
+        self.vq = rnd(self.vB, self.vn, self.Hq, 128)
+        self.vk = rnd(self.vB, self.vn, self.Hkv, 128)
+        self.vv = rnd(self.vB, self.vn, self.Hkv, 128)
+        self.vstart = torch.full((self.vB,), self.vL0, dtype=torch.int32,
+                                 device=dev)
+        self.vout = torch.empty((self.vB, self.vn, self.Hq, 128),
+                                dtype=torch.bfloat16, device=dev)
+        self.vws = qa.workspace(qa.QA_OP_VERIFY, self.vB, self.Hq, self.Hkv,
+                                self.vcap, self.vn)
+        torch.cuda.synchronize()
+        self.graph = None
+
+    # -- phases ---------------------------------------------------------------
+    def prefill_layer(self, l):
+        self.qa.prefill(self.caches[l], self.params, self.pq[l], self.pk[l],
+                        self.pv[l], self.cu, self.ppos, self.S, out=self.pout,
+                        ws=self.pws)
+
+    def prefill_all(self):
+        for l in range(self.L):
+            self.prefill_layer(l)
+
+    def decode_layer(self, l):
+        self.qa.decode(self.caches[l], self.params, self.dq[l], self.dk[l],
+                       self.dv[l], self.dpos, self.cap, out=self.dout,
+                       ws=self.dws)
+
+    def capture_decode_step(self):
+        torch = self.torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):  # warm the path outside the capture
+            for l in range(self.L):
+                self.decode_layer(l)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for l in range(self.L):
+                self.decode_layer(l)
+            self.dpos.add_(1)
+        torch.cuda.synchronize()
+        self.graph = g
+
+    def decode_all(self):
+        self.dpos.copy_(self.dpos0)
+        for _ in range(self.steps):
+            self.graph.replay()
+
+    def verify(self):
+        self.qa.verify(self.vcache, self.params, self.vq, self.vk, self.vv,
+                       self.vstart, self.vcap, out=self.vout, ws=self.vws)
+
+
+def decode_bytes(B, Hq, Hkv, ctx):
+    """Algorithmic HBM bytes of one decode launch at context ctx: K and V
+    reads of ctx slots, the new K/V slot writes, q reads and output writes."""
+    kv_read = 2 * B * Hkv * ctx * 128 * 2
+    kv_write = 2 * B * Hkv * 128 * 2
+    q_out = 2 * B * Hq * 128 * 2
+    return kv_read + kv_write + q_out
+
+
+def prefill_flops(B, Hq, S):
+    """Causal attention flops, lower triangle with the diagonal."""
+    return 2.0 * B * Hq * 128 * S * (S + 1)
+
+
+def time_kernels(wl, torch, reps):
+    """Live per-launch durations with events on the launch stream."""
+    st = torch.cuda.current_stream()
+    # decode at a fixed context (the mean of the 128-step sweep), over all 36
+    # layers in turn so no layer's cache is still in the last-level cache
+    wl.dpos.fill_(wl.S + wl.steps // 2)
+    ev = [(torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(wl.L * reps)]
+    i = 0
+    for _ in range(reps):
+        for l in range(wl.L):
+            ev[i][0].record(st)
+            wl.decode_layer(l)
+            ev[i][1].record(st)
+            i += 1
+    torch.cuda.synchronize()
+    dec_us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    # prefill: the whole qa_prefill call (prologue + attention) per layer
+    ev = [(torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(wl.L)]
+    for l in range(wl.L):
+        ev[l][0].record(st)
+        wl.prefill_layer(l)
+        ev[l][1].record(st)
+    torch.cuda.synchronize()
+    pre_us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    return dec_us, pre_us
+
+
+def cpu_baseline(budget_s=20.0):
+    """The fp64 oracle (as is) on a bounded sample of the same workload:
+    decode steps of the B=4, 2048-context layer shape, scaled to 36 layers."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    w = W.get(2)
+    B, Hq, Hkv, S, cap = w.batch, w.n_q_heads, w.n_kv_heads, 2048, w.capacity
+    c = oracle.Cache.empty(B, Hkv, cap, 128)
+    kk = W.normal_bf16((B, Hkv, S, 128), 2, 0, 0, "cache_k").double().numpy()
+    vv = W.normal_bf16((B, Hkv, S, 128), 2, 0, 0, "cache_v").double().numpy()
+    c.k[:, :, :S] = kk
+    c.v[:, :, :S] = vv
+    n = 0
+    t0 = time.perf_counter()
+    pos = np.full(B, S, dtype=np.int64)
+    while True:
+        q = W.normal_bf16((B, Hq, 128), 2, 1, n, "q").double().numpy()
+        k = W.normal_bf16((B, Hkv, 128), 2, 1, n, "k").double().numpy()
+        v = W.normal_bf16((B, Hkv, 128), 2, 1, n, "v").double().numpy()
+        _, _, c = oracle.decode(c, q, k, v, pos, scale=w.scale, theta=w.theta,
+                                eps=w.eps)
+        pos = pos + 1
+        n += 1
+        if time.perf_counter() - t0 > budget_s or n >= 64:
+            break
+    per_layer_us = (time.perf_counter() - t0) / n * 1e6
+    return {"value": per_layer_us * w.n_layers, "unit": "us/decode_step",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} single-layer decode calls at B=4, context "
+                      f"{S + 1}..{S + n} (fp64 numpy oracle), scaled x{w.n_layers} "
+                      f"layers"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=4)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the path runs on one device's "
+              f"share of the work; --gpus {args.gpus} is not supported",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads as W
+    from prefill_attention_rmsnorm_amd import qa
+
+    qa.lib()  # fails loudly if the HIP library is missing
+    torch.cuda.set_device(0)
+    wl = Workload(torch, qa, W)
+    log("bench: capturing the decode-step graph")
+    wl.capture_decode_step()
+
+    def step(evs=None):
+        if evs: evs[0].record()
+        wl.prefill_all()
+        if evs: evs[1].record()
+        wl.decode_all()
+        if evs: evs[2].record()
+        wl.verify()
+        if evs: evs[3].record()
+
+    for i in range(args.warmup):
+        log(f"bench: warmup step {i}")
+        step()
+    torch.cuda.synchronize()
+
+    phase = {"prefill": 0.0, "decode": 0.0, "verify": 0.0}
+    per_step = []
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        step(evs)
+        torch.cuda.synchronize()
+        p, d, v = (evs[0].elapsed_time(evs[1]), evs[1].elapsed_time(evs[2]),
+                   evs[2].elapsed_time(evs[3]))
+        phase["prefill"] += p
+        phase["decode"] += d
+        phase["verify"] += v
+        per_step.append(p + d + v)
+        log(f"bench: step {i}: prefill {p:.3f} ms, decode {d:.3f} ms, "
+            f"verify {v * 1e3:.1f} us")
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    K = args.steps
+    ms_per_step = sum(per_step) / K
+    pre_ms = phase["prefill"] / K
+    dec_ms = phase["decode"] / K
+    ver_us = phase["verify"] / K * 1e3
+
+    B, Hq, Hkv, S, L, NS = wl.B, wl.Hq, wl.Hkv, wl.S, wl.L, wl.steps
+    dec_us_step = dec_ms * 1e3 / NS
+    step_bytes = sum(decode_bytes(B, Hq, Hkv, S + 1 + s) for s in range(NS)) \
+        / NS * L
+    dec_gbps = step_bytes / (dec_us_step * 1e-6) / 1e9
+    pflops = prefill_flops(B, Hq, S)
+    pre_tflops = pflops * L / (pre_ms * 1e-3) / 1e12
+
+    log("bench: live per-launch timing")
+    dec_us, pre_us = time_kernels(wl, torch, args.kernel_reps)
+    dec_avg = sum(dec_us) / len(dec_us)
+    pre_avg = sum(pre_us) / len(pre_us)
+    ctx_fixed = S + NS // 2 + 1
+    dec_launch_bytes = decode_bytes(B, Hq, Hkv, ctx_fixed)
+    dec_ach = dec_launch_bytes / (dec_avg * 1e-6) / 1e9
+    pre_ach = pflops / (pre_avg * 1e-6) / 1e12
+
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            t = json.load(f)
+        if t.get("kernel_source_sha") == build_info().get("decode_source_sha"):
+            traffic = t.get("bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": round(dec_us_step, 3),
+        "unit": "us/decode_step",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "qwen3_4b_b4_s2048_36l", "batch": B,
+                   "prompt_len": S, "decode_steps": NS, "layers": L,
+                   "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": 128,
+                   "verify": {"batch": wl.vB, "block": wl.vn,
+                              "cache_slots": wl.vL0},
+                   "parallelism": "none (1 GPU)"},
+        "decode_us_per_step": round(dec_us_step, 3),
+        "decode_GBps": round(dec_gbps, 1),
+        "decode_frac_hbm_peak": round(dec_gbps / HBM_PEAK_GBPS, 4),
+        "prefill_ms_36_layers": round(pre_ms, 4),
+        "prefill_us_per_layer": round(pre_ms * 1e3 / L, 2),
+        "prefill_TFLOPs": round(pre_tflops, 1),
+        "prefill_frac_mfma_peak": round(pre_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "verify_us": round(ver_us, 2),
+        "roofline": {"kernel": "qa::decode_kernel<4,128>", "bound": "hbm",
+                     "achieved": round(dec_ach, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s",
+                     "frac": round(dec_ach / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": dec_launch_bytes,
+                     "avg_launch_us": round(dec_avg, 3),
+                     "launches_timed": len(dec_us)},
+        "roofline_prefill": {"kernels": "kv_prologue_kernel + "
+                             "prefill_attn_kernel<4>", "bound": "mfma",
+                             "achieved": round(pre_ach, 1),
+                             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(pre_ach / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "flops_per_launch": pflops,
+                             "avg_call_us": round(pre_avg, 2)},
+        "wall_s_timed": round(wall, 3),
+        "provenance": build_info(),
+    }
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (fp64 oracle, bounded sample)")
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -135,9 +135,9 @@ size_t qa_workspace_bytes(int op, int batch, int n_q_heads, int n_kv_heads,
                           int max_ctx, int block_len);
 
 /*
- * Clear a workspace (error word and merge counters) with a fill kernel on
- * stream s.  Must run once after allocating a workspace and before its first
- * use; the kernels leave the counters cleared after every call.
+ * Clear a workspace (its device error word) with a fill kernel on stream s.
+ * Run once after allocating a workspace, before its first use.  Split-K
+ * partials in the workspace are fully rewritten by every call.
  */
 qa_status qa_workspace_init(void* ws, size_t ws_bytes, void* stream);
 

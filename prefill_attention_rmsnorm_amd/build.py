@@ -7,6 +7,8 @@ disabled (``-packed-fp32-ops``) for all device code.
 
 from __future__ import annotations
 
+import hashlib
+import json
 import os
 import shutil
 import subprocess
@@ -20,7 +22,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqa.so")
 ARCH = "gfx950"
 
-SOURCES = ["qa_api.cpp", "util.hip", "prefill.hip", "decode.hip", "verify.hip"]
+SOURCES = ["qa_api.cpp", "util.hip", "prefill.hip", "decode.hip", "verify.hip",
+           "merge.hip"]
 HEADERS = ["qa_internal.h", "qa_device.h", "attn_tile.h"]
 
 
@@ -51,6 +54,43 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _sha(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _git(*args) -> str:
+    try:
+        r = subprocess.run(["git", "-C", ROOT] + list(args),
+                           capture_output=True, text=True, timeout=10)
+        return r.stdout.strip() if r.returncode == 0 else ""
+    except (OSError, subprocess.SubprocessError):
+        return ""
+
+
+def _write_build_info():
+    ver = subprocess.run([hipcc(), "--version"], capture_output=True,
+                         text=True).stdout.splitlines()
+    info = {
+        "commit": _git("rev-parse", "HEAD") or "unknown",
+        "dirty": _git("status", "--short", "--", "prefill_attention_rmsnorm_amd",
+                      "include"),
+        "hipcc": ver[0] if ver else "",
+        "arch": ARCH,
+        "decode_source_sha": _sha(["decode.hip", "merge.hip", "qa_device.h",
+                                   "qa_internal.h"]),
+        "prefill_source_sha": _sha(["prefill.hip", "attn_tile.h",
+                                    "qa_device.h", "qa_internal.h"]),
+        "verify_source_sha": _sha(["verify.hip", "attn_tile.h", "qa_device.h",
+                                   "qa_internal.h"]),
+    }
+    with open(os.path.join(BUILD, "BUILD_INFO.json"), "w") as f:
+        json.dump(info, f, indent=1)
+
+
 def build(verbose: bool = True) -> str:
     """Compile every source and link libqa.so; returns the library path."""
     os.makedirs(BUILD, exist_ok=True)
@@ -64,6 +104,7 @@ def build(verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stderr}")
     os.replace(tmp, LIB)
+    _write_build_info()
     if verbose:
         print(f"built {LIB}", file=sys.stderr)
     return LIB

@@ -34,8 +34,7 @@ __device__ __forceinline__ int key_of_reg(int r, int h2) {
   return 16 * (r >> 3) + 8 * h2 + (r & 7);
 }
 
-// Staging of one 64-key tile: global (or the LDS copy of freshly written
-// slots) -> registers -> LDS.  NT threads; K stays row-major (padded), V is
+// Staging of one 64-key tile: global -> registers -> LDS.  NT threads; K stays row-major (padded), V is
 // transposed to V^T[d][key] on the way into LDS.
 template <int NT>
 struct TileStage {
@@ -44,25 +43,17 @@ struct TileStage {
   u32x4 k[KPER];
   u32x4 v[VUNITS * 4];
 
-  // keys in [new0, new1) come from knew/vnew (LDS, [key-new0][128] bf16);
-  // keys >= kend are zero.
+  // Rows at or beyond kend are loaded from row kend-1 instead (a written
+  // slot; such keys are masked, so their V rows are multiplied by p = 0).
+  // The loads are unconditional so that all of them are in flight at once.
   __device__ __forceinline__ void load(const uint16_t* kbase,
                                        const uint16_t* vbase, int64_t sp,
-                                       int kv0, int kend, int new0, int new1,
-                                       const uint16_t* knew,
-                                       const uint16_t* vnew, int tid) {
+                                       int kv0, int kend, int tid) {
 #pragma unroll
     for (int i = 0; i < KPER; ++i) {
       const int ci = tid + NT * i;
-      const int key = kv0 + (ci >> 4), c = ci & 15;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (key < kend) {
-        if (key >= new0 && key < new1)
-          x = ld16(knew + (key - new0) * kHeadDim + 8 * c);
-        else
-          x = ld16(kbase + (size_t)key * sp + 8 * c);
-      }
-      k[i] = x;
+      const int key = min(kv0 + (ci >> 4), kend - 1), c = ci & 15;
+      k[i] = ld16(kbase + (size_t)key * sp + 8 * c);
     }
 #pragma unroll
     for (int u = 0; u < VUNITS; ++u) {
@@ -70,15 +61,8 @@ struct TileStage {
       const int kg = ui & 15, c = ui >> 4;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int key = kv0 + 4 * kg + i;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (key < kend) {
-          if (key >= new0 && key < new1)
-            x = ld16(vnew + (key - new0) * kHeadDim + 8 * c);
-          else
-            x = ld16(vbase + (size_t)key * sp + 8 * c);
-        }
-        v[4 * u + i] = x;
+        const int key = min(kv0 + 4 * kg + i, kend - 1);
+        v[4 * u + i] = ld16(vbase + (size_t)key * sp + 8 * c);
       }
     }
   }

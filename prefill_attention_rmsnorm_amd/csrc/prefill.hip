@@ -138,14 +138,14 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillArgs a) {
   WaveAttn st;
   st.init();
   TileStage<256> stage;
-  stage.load(kbase, vbase, a.c.sp, 0, kv_end, 0, 0, nullptr, nullptr, tid);
+  stage.load(kbase, vbase, a.c.sp, 0, kv_end, tid);
   stage.store(smem, tid);
   __syncthreads();
   for (int kt = 0; kt < n_kt; ++kt) {
     const int kv0 = kt * kKeyTile;
     if (kt + 1 < n_kt)
-      stage.load(kbase, vbase, a.c.sp, kv0 + kKeyTile, kv_end, 0, 0, nullptr,
-                 nullptr, tid);
+      stage.load(kbase, vbase, a.c.sp, kv0 + kKeyTile, kv_end, tid);
+    __builtin_amdgcn_sched_barrier(0);
     st.tile(smem + (kt & 1) * kStageBytes, qb, kv0, kv0 + kKeyTile - 1 > pmin,
             p, kv_end, j, h2);
     if (kt + 1 < n_kt) stage.store(smem + ((kt + 1) & 1) * kStageBytes, tid);

@@ -298,7 +298,6 @@ static qa_status fill_split_args(qa::DecodeArgs& a, const qa_cache* c,
   a.lse = lse;
   char* base = static_cast<char*>(ws);
   a.err = reinterpret_cast<int*>(base);
-  a.counters = reinterpret_cast<int*>(base + L.counters_off);
   a.part_m = reinterpret_cast<float*>(base + L.m_off);
   a.part_l = reinterpret_cast<float*>(base + L.l_off);
   a.part_o = reinterpret_cast<float*>(base + L.o_off);

@@ -64,6 +64,15 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
       __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// D(16x16 fp32) += A(16x32 bf16) * B(32x16 bf16).  Lane l holds
+// A[l%16][8*(l/16) .. +7], B[8*(l/16) .. +7][l%16], and D rows 4*(l/16) + r
+// of column l%16 for register r.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+      __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
 // ---- cross-lane ------------------------------------------------------------
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -84,6 +93,14 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp<kDppXor1>(x));
+  x = fmaxf(x, dpp<kDppXor2>(x));
+  x = fmaxf(x, dpp<kDppHalfMirror>(x));
+  x = fmaxf(x, dpp<kDppMirror>(x));
+  return x;
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
   return x;
@@ -99,6 +116,68 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
 }
 __device__ __forceinline__ void st16(void* p, u32x4 v) {
   *reinterpret_cast<u32x4*>(p) = v;
+}
+
+// cos/sin of an fp64 angle in fp32: Cody-Waite reduction by 2*pi in fp64,
+// then the fp32 library sincos on |r| <= pi (query side, where the result is
+// rounded to bf16 anyway).
+__device__ __forceinline__ void sincos_reduced(double a, float* s, float* c) {
+  const double k = rint(a * 0.15915494309189535);
+  double r = fma(-k, 6.283185307179586, a);
+  r = fma(-k, 2.4492935982947064e-16, r);
+  sincosf((float)r, s, c);
+}
+
+// Log-sum-exp merge of n_split partial rows (m: max in log2 units, l: sum,
+// o: unnormalised output) for 4 consecutive dims of one row.  Loads are
+// issued 16 splits at a time so that a merge costs one memory round trip per
+// 16 splits.  stride_row: floats between consecutive splits of m/l (= rows).
+struct MergeOut {
+  float m, l;
+  float4 o;
+};
+__device__ __forceinline__ MergeOut merge_splits(const float* pm, const float* pl,
+                                                 const float* po, int n_split,
+                                                 int rows) {
+  const float ninf = -__builtin_inff();
+  MergeOut r;
+  r.m = ninf;
+  r.l = 0.f;
+  r.o = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < n_split; s0 += 16) {
+    float mv[16], lv[16];
+    float4 ov[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const int s = s0 + c;
+      mv[c] = ninf;
+      lv[c] = 0.f;
+      ov[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (s < n_split) {
+        mv[c] = pm[(size_t)s * rows];
+        lv[c] = pl[(size_t)s * rows];
+        ov[c] = *reinterpret_cast<const float4*>(po + (size_t)s * rows * kHeadDim);
+      }
+    }
+    float mc = ninf;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) mc = fmaxf(mc, mv[c]);
+    const float mn = fmaxf(r.m, mc);
+    if (mn == ninf) continue;
+    const float alpha = (r.m == ninf) ? 0.f : __builtin_amdgcn_exp2f(r.m - mn);
+    r.l *= alpha;
+    r.o.x *= alpha; r.o.y *= alpha; r.o.z *= alpha; r.o.w *= alpha;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      if (mv[c] == ninf) continue;
+      const float wgt = __builtin_amdgcn_exp2f(mv[c] - mn);
+      r.l += wgt * lv[c];
+      r.o.x += wgt * ov[c].x; r.o.y += wgt * ov[c].y;
+      r.o.z += wgt * ov[c].z; r.o.w += wgt * ov[c].w;
+    }
+    r.m = mn;
+  }
+  return r;
 }
 
 __device__ __forceinline__ void flag_error(int* err, int bits) {

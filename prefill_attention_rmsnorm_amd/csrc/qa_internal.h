@@ -21,8 +21,7 @@ struct RopeFreq {
 // ---- workspace layout --------------------------------------------------------
 //   [0, 256)                 int32 error word at 0
 //   prefill: + cos/sin table float2 [total_tokens][64]
-//   decode / verify: + int32 merge counters [batch*n_kv_heads] (256-B rounded)
-//                    + fp32 m, l [batch][n_kv][n_split][rows] each
+//   decode / verify: + fp32 m, l [batch][n_kv][n_split][rows] each
 //                    + fp32 o   [batch][n_kv][n_split][rows][128]
 // rows = G (decode) or block_len*G (verify).
 inline size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -30,7 +29,7 @@ inline size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 struct SplitLayout {
   int keys_per_split;
   int n_split;
-  size_t counters_off, m_off, l_off, o_off, total;
+  size_t m_off, l_off, o_off, total;
 };
 
 // Decode: keys per split-K block.  Small grids use short splits so more
@@ -61,8 +60,7 @@ inline SplitLayout split_layout(int batch, int n_kv, int rows, int max_ctx,
   if (L.n_split < 1) L.n_split = 1;
   size_t pairs = (size_t)batch * n_kv;
   size_t nrow = pairs * L.n_split * rows;
-  L.counters_off = kWsHeader;
-  L.m_off = L.counters_off + round256(pairs * sizeof(int));
+  L.m_off = kWsHeader;
   L.l_off = L.m_off + round256(nrow * sizeof(float));
   L.o_off = L.l_off + round256(nrow * sizeof(float));
   L.total = L.o_off + round256(nrow * kHeadDim * sizeof(float));
@@ -117,7 +115,6 @@ struct DecodeArgs {
   uint16_t* out;
   float* lse;
   int* err;
-  int* counters;
   float* part_m;
   float* part_l;
   float* part_o;
@@ -130,6 +127,7 @@ hipError_t launch_decode(const DecodeArgs& a, const RopeFreq& f, int group,
                          hipStream_t s, int* n_kernels);
 hipError_t launch_verify(const DecodeArgs& a, const RopeFreq& f, int group,
                          hipStream_t s, int* n_kernels);
+hipError_t launch_merge(const DecodeArgs& a, int group, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 

@@ -5,8 +5,8 @@
 // must equal what sequential decode steps would give.  The draft's
 // block_len tokens x G heads of one KV head form up to 128 query rows that
 // share every K/V tile (MFMA tile machinery of the prefill kernel); the keys
-// are split across workgroups, and the last workgroup of each
-// (sequence, kv head) merges the partials in split order.
+// are split across workgroups, each writing a partial that merge.hip
+// combines in split order.
 //
 // The workgroup whose key range holds some of the new slots first runs the
 // prologue for them (k' in fp64 with one RNE) and writes them to the cache;
@@ -21,7 +21,6 @@ template <int G, int NW>
 __global__ __launch_bounds__(NW * 64) void verify_kernel(DecodeArgs a, RopeFreq f) {
   constexpr int NT = NW * 64;
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStageBytes];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int j = l & 31, h2 = l >> 5;
@@ -89,14 +88,14 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(DecodeArgs a, RopeFreq 
     WaveAttn st;
     st.init();
     TileStage<NT> stage;
-    stage.load(kbase, vbase, a.c.sp, k0, k1, 0, 0, nullptr, nullptr, tid);
+    stage.load(kbase, vbase, a.c.sp, k0, k1, tid);
     stage.store(smem, tid);
     __syncthreads();
     for (int kt = 0; kt < n_kt; ++kt) {
       const int kv0 = k0 + kt * kKeyTile;
       if (kt + 1 < n_kt)
-        stage.load(kbase, vbase, a.c.sp, kv0 + kKeyTile, k1, 0, 0, nullptr,
-                   nullptr, tid);
+        stage.load(kbase, vbase, a.c.sp, kv0 + kKeyTile, k1, tid);
+      __builtin_amdgcn_sched_barrier(0);
       const bool need_mask = (kv0 + kKeyTile > k1) || (kv0 + kKeyTile - 1 > L0);
       st.tile(smem + (kt & 1) * kStageBytes, qb, kv0, need_mask,
               row_ok ? p : -1, k1, j, h2);
@@ -126,52 +125,6 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(DecodeArgs a, RopeFreq 
     }
   }
 
-  // ---- the last workgroup of this (sequence, kv head) merges the splits
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int prev = __hip_atomic_fetch_add(a.counters + pairidx, 1, __ATOMIC_ACQ_REL,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (prev == a.n_split - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-
-  const size_t pbase = pairidx * a.n_split * rows;
-  for (int idx = tid; idx < rows * (kHeadDim / 4); idx += NT) {
-    const int rr = idx / (kHeadDim / 4), d4 = (idx % (kHeadDim / 4)) * 4;
-    float Mx = -__builtin_inff();
-    for (int s = 0; s < a.n_split; ++s) Mx = fmaxf(Mx, a.part_m[pbase + s * rows + rr]);
-    float L = 0.f;
-    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (Mx != -__builtin_inff()) {
-      for (int s = 0; s < a.n_split; ++s) {
-        const float ms = a.part_m[pbase + s * rows + rr];
-        if (ms == -__builtin_inff()) continue;
-        const float wgt = __builtin_amdgcn_exp2f(ms - Mx);
-        L += wgt * a.part_l[pbase + s * rows + rr];
-        const float4 po = *reinterpret_cast<const float4*>(
-            a.part_o + (pbase + s * rows + rr) * kHeadDim + d4);
-        O.x += wgt * po.x; O.y += wgt * po.y; O.z += wgt * po.z; O.w += wgt * po.w;
-      }
-    }
-    const bool good = ok && L > 0.f;
-    const float inv = good ? 1.0f / L : 0.f;
-    const int rhl = rr / n, rti = rr % n;
-    const size_t orow = (((size_t)b * n + rti) * a.n_q_heads + g * G + rhl) * kHeadDim;
-    u32x2 pr = {0u, 0u};
-    if (good) {
-      pr[0] = pack_bf16x2(O.x * inv, O.y * inv);
-      pr[1] = pack_bf16x2(O.z * inv, O.w * inv);
-    }
-    *reinterpret_cast<u32x2*>(a.out + orow + d4) = pr;
-    if (a.lse && d4 == 0)
-      a.lse[((size_t)b * n + rti) * a.n_q_heads + g * G + rhl] =
-          good ? (Mx + __log2f(L)) * kLn2 : 0.f;
-  }
-  if (tid == 0)
-    __hip_atomic_store(a.counters + pairidx, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int G>
@@ -201,7 +154,10 @@ hipError_t launch_verify(const DecodeArgs& a, const RopeFreq& f, int group,
     case 8: e = launch_verify_g<8>(a, f, s); break;
     default: return hipErrorInvalidValue;
   }
-  if (e == hipSuccess) *n_kernels = 1;
+  if (e != hipSuccess) return e;
+  *n_kernels = 1;
+  e = launch_merge(a, group, s);
+  if (e == hipSuccess) *n_kernels = 2;
   return e;
 }
 
