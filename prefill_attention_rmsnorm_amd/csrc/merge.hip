@@ -22,7 +22,7 @@ __global__ __launch_bounds__(128) void merge_kernel(DecodeArgs a, int G) {
   const int b = pair / a.n_kv_heads, g = pair % a.n_kv_heads;
   const int rr = item >> 5, d4 = (item & 31) * 4;
   const size_t r0 = (size_t)pair * a.n_split * rows + rr;
-  const MergeOut mo = merge_splits(a.part_m + r0, a.part_l + r0,
+  const MergeOut mo = merge_splits<32>(a.part_m + r0, a.part_l + r0,
                                    a.part_o + r0 * kHeadDim + d4, a.n_split, rows);
   const bool good = mo.l > 0.f;
   const float inv = good ? 1.0f / mo.l : 0.f;

@@ -130,12 +130,13 @@ __device__ __forceinline__ void sincos_reduced(double a, float* s, float* c) {
 
 // Log-sum-exp merge of n_split partial rows (m: max in log2 units, l: sum,
 // o: unnormalised output) for 4 consecutive dims of one row.  Loads are
-// issued 16 splits at a time so that a merge costs one memory round trip per
-// 16 splits.  stride_row: floats between consecutive splits of m/l (= rows).
+// issued CH splits at a time so that a merge costs one memory round trip per
+// CH splits.  stride_row: floats between consecutive splits of m/l (= rows).
 struct MergeOut {
   float m, l;
   float4 o;
 };
+template <int CH = 16>
 __device__ __forceinline__ MergeOut merge_splits(const float* pm, const float* pl,
                                                  const float* po, int n_split,
                                                  int rows) {
@@ -144,11 +145,11 @@ __device__ __forceinline__ MergeOut merge_splits(const float* pm, const float* p
   r.m = ninf;
   r.l = 0.f;
   r.o = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < n_split; s0 += 16) {
-    float mv[16], lv[16];
-    float4 ov[16];
+  for (int s0 = 0; s0 < n_split; s0 += CH) {
+    float mv[CH], lv[CH];
+    float4 ov[CH];
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
+    for (int c = 0; c < CH; ++c) {
       const int s = s0 + c;
       mv[c] = ninf;
       lv[c] = 0.f;
@@ -161,14 +162,14 @@ __device__ __forceinline__ MergeOut merge_splits(const float* pm, const float* p
     }
     float mc = ninf;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) mc = fmaxf(mc, mv[c]);
+    for (int c = 0; c < CH; ++c) mc = fmaxf(mc, mv[c]);
     const float mn = fmaxf(r.m, mc);
     if (mn == ninf) continue;
     const float alpha = (r.m == ninf) ? 0.f : __builtin_amdgcn_exp2f(r.m - mn);
     r.l *= alpha;
     r.o.x *= alpha; r.o.y *= alpha; r.o.z *= alpha; r.o.w *= alpha;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
+    for (int c = 0; c < CH; ++c) {
       if (mv[c] == ninf) continue;
       const float wgt = __builtin_amdgcn_exp2f(mv[c] - mn);
       r.l += wgt * lv[c];
