@@ -68,7 +68,6 @@ template <int G>
 __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillArgs a) {
   constexpr int TQ = 128 / G;
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStageBytes];
-  __shared__ int s_kv_end, s_pmin;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int j = l & 31, h2 = l >> 5;
@@ -102,14 +101,32 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillArgs a) {
   const int h = g * G + hl;
   const bool tok_ok = tl < n_tok;
   const int t = tok0 + tl;
-  int p = tok_ok ? a.positions[t] : -1;
-  const bool q_ok = tok_ok && p >= 0 && p < a.c.capacity;
 
-  if (tid == 0) { s_kv_end = 0; s_pmin = INT_MAX; }
-  __syncthreads();
-  if (q_ok) { atomicMax(&s_kv_end, p + 1); atomicMin(&s_pmin, p); }
-  __syncthreads();
-  const int kv_end = s_kv_end, pmin = s_pmin;
+  // Positions of the block's tokens: every wave reads all of them (TQ <= 128)
+  // and reduces in registers, so no LDS round trip or barrier is needed.
+  // The q-side reads go out together with them.
+  int pv0 = -1, pv1 = -1;
+  if (l < n_tok) pv0 = a.positions[tok0 + l];
+  if (TQ > 64 && l + 64 < n_tok) pv1 = a.positions[tok0 + l + 64];
+  QPrologue qp;
+  qp.load(a.q + (size_t)t * a.q_tok_stride + (size_t)h * kHeadDim, tok_ok,
+          a.cs + (size_t)(tok_ok ? t : 0) * kHalf, a.q_norm_w, h2);
+
+  const int cap = a.c.capacity;
+  const bool v0 = pv0 >= 0 && pv0 < cap, v1 = pv1 >= 0 && pv1 < cap;
+  int kv_end = max(v0 ? pv0 + 1 : 0, v1 ? pv1 + 1 : 0);
+  int pmin = min(v0 ? pv0 : INT_MAX, v1 ? pv1 : INT_MAX);
+#pragma unroll
+  for (int sh = 1; sh < 64; sh <<= 1) {
+    kv_end = max(kv_end, __shfl_xor(kv_end, sh));
+    pmin = min(pmin, __shfl_xor(pmin, sh));
+  }
+  // wave-uniform (the tile loader's buffer descriptors must live in SGPRs)
+  kv_end = __builtin_amdgcn_readfirstlane(kv_end);
+  pmin = __builtin_amdgcn_readfirstlane(pmin);
+  const int pa = __shfl(pv0, tl & 63), pb = __shfl(pv1, tl & 63);
+  int p = !tok_ok ? -1 : (tl < 64 ? pa : pb);
+  const bool q_ok = tok_ok && p >= 0 && p < cap;
   if (!q_ok) p = kv_end - 1;  // sees every key; its output is not kept
 
   uint16_t* orow = a.out + ((size_t)t * a.n_q_heads + h) * kHeadDim;
@@ -126,29 +143,29 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillArgs a) {
     return;
   }
 
-  u32x4 qb[8];
-  q_prologue(a.q + (size_t)t * a.q_tok_stride + (size_t)h * kHeadDim, tok_ok,
-             a.cs + (size_t)(tok_ok ? t : 0) * kHalf, a.q_norm_w, (float)a.eps,
-             a.qscale, h2, qb);
-
   const uint16_t* kbase = a.c.k + (size_t)seq * a.c.sb + (size_t)g * a.c.sh;
   const uint16_t* vbase = a.c.v + (size_t)seq * a.c.sb + (size_t)g * a.c.sh;
   const int n_kt = (kv_end + kKeyTile - 1) / kKeyTile;
 
+  TileLoader<4> ld;
+  ld.init(__builtin_amdgcn_readfirstlane(w), l, a.c.sp);
+  ld.load(kbase, vbase, a.c.sp, 0, kv_end, smem);
+
+  u32x4 qb[8];
+  qp.compute((float)a.eps, a.qscale, qb);
+
   WaveAttn st;
-  st.init();
-  TileStage<256> stage;
-  stage.load(kbase, vbase, a.c.sp, 0, kv_end, tid);
-  stage.store(smem, tid);
+  st.init(l);
+  wait_tile_loads();
   __syncthreads();
   for (int kt = 0; kt < n_kt; ++kt) {
     const int kv0 = kt * kKeyTile;
+    // the stage written here was last read in iteration kt-1, before the barrier
     if (kt + 1 < n_kt)
-      stage.load(kbase, vbase, a.c.sp, kv0 + kKeyTile, kv_end, tid);
-    __builtin_amdgcn_sched_barrier(0);
-    st.tile(smem + (kt & 1) * kStageBytes, qb, kv0, kv0 + kKeyTile - 1 > pmin,
-            p, kv_end, j, h2);
-    if (kt + 1 < n_kt) stage.store(smem + ((kt + 1) & 1) * kStageBytes, tid);
+      ld.load(kbase, vbase, a.c.sp, kv0 + kKeyTile, kv_end,
+              smem + ((kt + 1) & 1) * kStageBytes);
+    st.tile(smem + (kt & 1) * kStageBytes, qb, kv0, kv0 + kKeyTile - 1 > pmin, p, h2);
+    wait_tile_loads();
     __syncthreads();
   }
 

@@ -64,6 +64,10 @@ qa_status check_cache(const qa_cache* c) {
              QA_ERR_SHAPE, "cache strides too small");
   QA_REQUIRE(c->stride_pos % 8 == 0 && c->stride_h % 8 == 0 && c->stride_b % 8 == 0,
              QA_ERR_ALIGN, "cache strides must be multiples of 8 elements");
+  // a 64-key tile is addressed with 32-bit byte offsets from its first row
+  QA_REQUIRE(c->stride_pos <= qa::kMaxStridePos, QA_ERR_SHAPE,
+             "cache stride_pos %lld exceeds %lld elements", (long long)c->stride_pos,
+             (long long)qa::kMaxStridePos);
   return QA_OK;
 }
 

@@ -72,6 +72,10 @@ inline size_t prefill_ws_bytes(int total_tokens) {
 }
 
 // ---- kernel argument blocks ----------------------------------------------------
+// Largest cache stride_pos (elements): 64 rows of a key tile must span less
+// than 2^31 bytes so the tile loader's per-lane offsets fit 32 bits.
+constexpr int64_t kMaxStridePos = int64_t(1) << 23;
+
 struct CacheArgs {
   uint16_t* k;
   uint16_t* v;

@@ -77,29 +77,34 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(DecodeArgs a, RopeFreq 
     }
     __syncthreads();
     u32x4 qb[8];
-    q_prologue(a.q + (((size_t)b * n + ti) * a.n_q_heads + h) * kHeadDim,
-               row_ok && ok, cs + ti * kHalf, a.q_norm_w, (float)a.eps,
-               a.qscale, h2, qb);
+    {
+      QPrologue qp;
+      qp.load(a.q + (((size_t)b * n + ti) * a.n_q_heads + h) * kHeadDim,
+              row_ok && ok, cs + ti * kHalf, a.q_norm_w, h2);
+      qp.compute((float)a.eps, a.qscale, qb);
+    }
     __syncthreads();  // cs and the new slots' cache writes are done
 
     const uint16_t* kbase = a.c.k + (size_t)b * a.c.sb + (size_t)g * a.c.sh;
     const uint16_t* vbase = a.c.v + (size_t)b * a.c.sb + (size_t)g * a.c.sh;
     const int n_kt = (k1 - k0 + kKeyTile - 1) / kKeyTile;
+    TileLoader<NW> ld;
+    ld.init(__builtin_amdgcn_readfirstlane(w), l, a.c.sp);
     WaveAttn st;
-    st.init();
-    TileStage<NT> stage;
-    stage.load(kbase, vbase, a.c.sp, k0, k1, tid);
-    stage.store(smem, tid);
+    st.init(l);
+    // the cs table in LDS is dead after the barrier above
+    ld.load(kbase, vbase, a.c.sp, k0, k1, smem);
+    wait_tile_loads();
     __syncthreads();
+    const int lim_abs = row_ok ? min(p, k1 - 1) : k1 - 1;
     for (int kt = 0; kt < n_kt; ++kt) {
       const int kv0 = k0 + kt * kKeyTile;
       if (kt + 1 < n_kt)
-        stage.load(kbase, vbase, a.c.sp, kv0 + kKeyTile, k1, tid);
-      __builtin_amdgcn_sched_barrier(0);
+        ld.load(kbase, vbase, a.c.sp, kv0 + kKeyTile, k1,
+                smem + ((kt + 1) & 1) * kStageBytes);
       const bool need_mask = (kv0 + kKeyTile > k1) || (kv0 + kKeyTile - 1 > L0);
-      st.tile(smem + (kt & 1) * kStageBytes, qb, kv0, need_mask,
-              row_ok ? p : -1, k1, j, h2);
-      if (kt + 1 < n_kt) stage.store(smem + ((kt + 1) & 1) * kStageBytes, tid);
+      st.tile(smem + (kt & 1) * kStageBytes, qb, kv0, need_mask, lim_abs, h2);
+      wait_tile_loads();
       __syncthreads();
     }
     if (row_ok) {
