@@ -25,12 +25,21 @@ namespace qa {
 
 constexpr int kRowBytes = kHeadDim * 2;                   // 256
 constexpr int kKTileBytes = kKeyTile * kRowBytes;         // 16384
-constexpr int kStageBytes = 2 * kKTileBytes;              // K then V: 32768
+// One LDS stage holds a K tile and then a V tile.
+constexpr int kStageBytes = 2 * kKTileBytes;
 constexpr float kRescaleSlack = 8.0f;  // log2 units a stale max may lag by
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// max(a, b, c) with one v_max3_f32 (IEEE maxNum on quiet values; inputs here
+// are finite scores or -inf).
+__device__ __forceinline__ float max3_f32(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 
 // A-operand row i of the QK product holds key sigma(i) of a 32-key block:
 // S^T register r of lane half h2 then holds key 16*(r/8) + 8*h2 + r%8, which
@@ -47,12 +56,12 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
 }
 
-// Global -> LDS copy of one 64-key K/V tile by the NW waves of a workgroup.
-// A stage is 32 one-KiB pieces (16 of K, 16 of V), each 4 rows; wave w moves
-// pieces w, w + NW, ...  Lane L of a piece lands at LDS byte 16*L of it.
+// Global -> LDS copy of a 64-key K or V tile by the NW waves of a workgroup.
+// A tile is 16 one-KiB pieces of 4 rows; wave w moves pieces w, w + NW, ...
+// Lane L of a piece lands at LDS byte 16*L of it.
 template <int NW>
 struct TileLoader {
-  static constexpr int NI = 16 / NW;  // K (and V) pieces per wave
+  static constexpr int NI = 16 / NW;  // pieces per wave and tile
   uint32_t koff[NI], voff[NI];        // per-lane byte offsets from the tile's row 0
   int w;                              // wave index (uniform)
 
@@ -69,26 +78,28 @@ struct TileLoader {
     }
   }
 
-  // Keys kv0 .. kv0+63 of the rows at kbase/vbase (element stride sp); keys at
-  // or beyond kend read as zero.
-  __device__ __forceinline__ void load(const uint16_t* kbase, const uint16_t* vbase,
-                                       int64_t sp, int kv0, int kend,
-                                       unsigned char* stage) const {
+  // Rows kv0 .. kv0+63 of the row array at base (element stride sp) into the
+  // LDS tile dst; rows at or beyond kend read as zero.
+  __device__ __forceinline__ void load(const uint16_t* base, int64_t sp, int kv0,
+                                       int kend, unsigned char* dst,
+                                       const uint32_t (&off)[NI]) const {
     const int nrows = min(max(kend - kv0, 0), kKeyTile);
     // < 2^31 since sp <= kMaxStridePos; readfirstlane keeps the descriptor
     // in SGPRs (a VALU min/max would otherwise force a waterfall loop)
     const int nrec = __builtin_amdgcn_readfirstlane(nrows * (int)sp * 2);
-    const size_t off = (size_t)kv0 * (size_t)sp;
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + off), 0, nrec, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + off), 0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(base + (size_t)kv0 * (size_t)sp), 0, nrec, 0x00020000);
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      buffer_load_lds16(rk, stage + (w + NW * i) * 1024, koff[i]);
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-      buffer_load_lds16(rv, stage + kKTileBytes + (w + NW * i) * 1024, voff[i]);
+      buffer_load_lds16(rs, dst + (w + NW * i) * 1024, off[i]);
+  }
+  __device__ __forceinline__ void load_k(const uint16_t* kbase, int64_t sp, int kv0,
+                                         int kend, unsigned char* dst) const {
+    load(kbase, sp, kv0, kend, dst, koff);
+  }
+  __device__ __forceinline__ void load_v(const uint16_t* vbase, int64_t sp, int kv0,
+                                         int kend, unsigned char* dst) const {
+    load(vbase, sp, kv0, kend, dst, voff);
   }
 };
 
@@ -102,8 +113,8 @@ struct WaveAttn {
   f32x16 o[4];  // O^T, d-block db: rows d = 32*db + 8*(r/4) + 4*h2 + r%4
   float m;      // running (possibly stale) max, log2 domain, per query
   float lsum;   // sum of this lane's half of the bf16-rounded probabilities
-  uint32_t kaddr[8];  // LDS byte offsets of this lane's K operand per k-step
-  uint32_t vaddr[4];  // LDS byte offsets of this lane's V^T piece per d-block
+  uint32_t kb;  // LDS byte offset of this lane's K operand at k-step 0
+  uint32_t vb;  // LDS byte offset of this lane's V^T piece at d-block 0
 
   __device__ __forceinline__ void init(int lane) {
 #pragma unroll
@@ -114,44 +125,103 @@ struct WaveAttn {
     lsum = 0.f;
     const int j = lane & 31, h2 = lane >> 5;
     // K operand: row sigma(j) (+32 for the second 32-key block), dims
-    // 16*kstep + 8*h2 .. +7 = logical chunk 2*kstep + h2.
+    // 16*kstep + 8*h2 .. +7 = logical chunk 2*kstep + h2, stored at chunk
+    // (2*kstep + h2) ^ (row & 15); the k-step enters as an XOR of 32*kstep.
     const int sj = sigma_row(j);
-    const int y = (sj & 15) ^ h2;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      kaddr[ks] = (uint32_t)(sj * kRowBytes + ((y ^ (2 * ks)) << 4));
+    kb = (uint32_t)(sj * kRowBytes + ((((sj & 15) ^ h2)) << 4));
     // V^T operand through ds_read_b64_tr_b16: in each 16-lane group, lane s
     // reads 4 dims of key row (base + s/4); the transpose hands lane i of the
     // group dim (i) of those 4 consecutive keys.  Group g16 covers dims
     // 16*(g16&1) .. +15 of the d-block and keys 8*(g16>>1) .. +3 (+4 for the
-    // second read).
+    // second read).  Logical chunk 4*db + x of row r sits at chunk
+    // (4*db + x) ^ (4*(r&3)); the d-block enters as an XOR of 64*db.
     const int g16 = lane >> 4, s = lane & 15, e = s >> 2, r4 = s & 3;
     const int x = 2 * (g16 & 1) + (r4 >> 1);
-    const uint32_t vb = (uint32_t)((8 * (g16 >> 1) + e) * kRowBytes + 16 * x + 8 * (r4 & 1));
-#pragma unroll
-    for (int db = 0; db < 4; ++db) vaddr[db] = vb + 64u * (uint32_t)(db ^ e);
+    vb = (uint32_t)((8 * (g16 >> 1) + e) * kRowBytes + 64 * e + 16 * x + 8 * (r4 & 1));
   }
 
-  // One 64-key tile held in LDS `stage`.  qb: Q'^T operand (8 k-steps).
-  // When need_mask, key kv0 + x counts only if kv0 + x <= lim_abs, where
-  // lim_abs = min(query position, last valid key).
+  // One 64-key tile in LDS: K at stage, V at stage + kKTileBytes.
+  // All K operand reads are issued before the QK MFMAs and all V^T reads
+  // before the softmax, so LDS latency is paid about once per phase.
+  // With MASK, key kv0 + x counts only if kv0 + x <= lim_abs, where
+  // lim_abs = min(query position, last valid key).  (A separate instantiation
+  // keeps the unmasked scores straight from the MFMA, which lets the max run
+  // as v_max3 without quieting every input first.)
+  template <bool MASK>
   __device__ __forceinline__ void tile(const unsigned char* stage,
                                        const u32x4 (&qb)[8], int kv0,
-                                       bool need_mask, int lim_abs, int h2) {
-    const unsigned char* ks = stage;
-    const unsigned char* vs = stage + kKTileBytes;
+                                       int lim_abs, int h2) {
+    // Re-derive the per-k-step and per-d-block LDS offsets inside each tile
+    // (one XOR each) instead of keeping a dozen of them live across the loop.
+    uint32_t kbt = kb, vbt = vb;
+    asm volatile("" : "+v"(kbt), "+v"(vbt));
+    // K operands in a ring of 4 k-steps: reads run two k-steps ahead of use
+    u32x4 ka[8];
+    read_k(stage, kbt, 0, ka[0], ka[1]);
+    read_k(stage, kbt, 1, ka[2], ka[3]);
+    read_k(stage, kbt, 2, ka[4], ka[5]);
+    read_k(stage, kbt, 3, ka[6], ka[7]);
+    __builtin_amdgcn_sched_barrier(0);
     f32x16 s0, s1;
 #pragma unroll
     for (int r = 0; r < 16; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
 #pragma unroll
-    for (int kstep = 0; kstep < 8; ++kstep) {
-      const u32x4 a0 = *reinterpret_cast<const u32x4*>(ks + kaddr[kstep]);
-      const u32x4 a1 = *reinterpret_cast<const u32x4*>(ks + 32 * kRowBytes + kaddr[kstep]);
-      s0 = mfma32x32x16(a0, qb[kstep], s0);
-      s1 = mfma32x32x16(a1, qb[kstep], s1);
+    for (int kstep = 0; kstep < 8; kstep += 2) {
+      const int u = (kstep & 3) * 2;  // ring slot of this k-step pair
+      s0 = mfma32x32x16(ka[u], qb[kstep], s0);
+      s1 = mfma32x32x16(ka[u + 1], qb[kstep], s1);
+      s0 = mfma32x32x16(ka[u + 2], qb[kstep + 1], s0);
+      s1 = mfma32x32x16(ka[u + 3], qb[kstep + 1], s1);
+      if (kstep + 4 < 8) {
+        read_k(stage, kbt, kstep + 4, ka[u], ka[u + 1]);
+        read_k(stage, kbt, kstep + 5, ka[u + 2], ka[u + 3]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    u32x4 va[16];  // [db][c]; d-blocks 0-1 before the softmax, 2-3 after
+    read_vt(stage, vbt, 0, va);
+    read_vt(stage, vbt, 1, va);
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 pb[4];
+    softmax<MASK>(s0, s1, kv0, lim_abs, h2, pb);
+    __builtin_amdgcn_sched_barrier(0);
+    read_vt(stage, vbt, 2, va);
+    read_vt(stage, vbt, 3, va);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[db] = mfma32x32x16(va[4 * db + c], pb[c], o[db]);
+  }
+
+  // K operand of one k-step for keys 0-31 (a0) and 32-63 (a1).
+  __device__ __forceinline__ static void read_k(const unsigned char* stage, uint32_t kbt,
+                                                int kstep, u32x4& a0, u32x4& a1) {
+    const uint32_t off = kbt ^ (32u * kstep);
+    a0 = *reinterpret_cast<const u32x4*>(stage + off);
+    a1 = *reinterpret_cast<const u32x4*>(stage + off + 32 * kRowBytes);
+  }
+
+  // V^T operand of d-block db for the four 16-key chunks (two transposing
+  // reads of 4 keys each per chunk, landing in the two halves of one operand).
+  __device__ __forceinline__ static void read_vt(const unsigned char* stage, uint32_t vbt,
+                                                 int db, u32x4 (&va)[16]) {
+    const uint32_t vo = kKTileBytes + (vbt ^ (64u * db));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(stage + vo + 16 * c * kRowBytes));
+      const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(stage + vo + (16 * c + 4) * kRowBytes));
+      va[4 * db + c] = __builtin_bit_cast(u32x4, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  }
+
+  // Online softmax of one tile's scores into bf16 P^T (pb[c]: keys 16c..16c+15).
+  template <bool MASK>
+  __device__ __forceinline__ void softmax(f32x16& s0, f32x16& s1, int kv0,
+                                          int lim_abs, int h2, u32x4 (&pb)[4]) {
     const float ninf = -__builtin_inff();
-    if (need_mask) {
+    if (MASK) {
       const int lim = lim_abs - kv0 - 8 * h2;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -160,9 +230,10 @@ struct WaveAttn {
         s1[r] = (kr + 32 > lim) ? ninf : s1[r];
       }
     }
+    // v_max3 straight on the scores (fmaxf would first quiet every input)
     float mt = ninf;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, fmaxf(s0[r], s1[r]));
+    for (int r = 0; r < 16; ++r) mt = max3_f32(mt, s0[r], s1[r]);
     // The max is refreshed only when a score passes the stale one by more
     // than kRescaleSlack, so p <= 2^kRescaleSlack and the O rescale is rare.
     if (__any(mt > m + kRescaleSlack)) {
@@ -170,14 +241,11 @@ struct WaveAttn {
       // a row with no visible key so far keeps m = -inf (o and lsum are 0)
       const float alpha = (mn == ninf) ? 1.f : __builtin_amdgcn_exp2f(m - mn);
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      for (int db = 0; db < 4; ++db) o[db] = o[db] * alpha;
       lsum *= alpha;
       m = mn;
     }
     const float mu = (m == ninf) ? 0.f : m;
-    u32x4 pb[4];
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
       pb[r >> 3][(r & 7) >> 1] = pack_bf16x2(__builtin_amdgcn_exp2f(s0[r] - mu),
@@ -190,23 +258,73 @@ struct WaveAttn {
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int i = 0; i < 4; ++i) lsum = dot2_bf16(pb[c][i], kOnes, lsum);
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(vs + vaddr[db] + 16 * c * kRowBytes));
-        const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(vs + vaddr[db] + (16 * c + 4) * kRowBytes));
-        const u32x2 w0 = __builtin_bit_cast(u32x2, t0);
-        const u32x2 w1 = __builtin_bit_cast(u32x2, t1);
-        u32x4 va;
-        va[0] = w0[0]; va[1] = w0[1]; va[2] = w1[0]; va[3] = w1[1];
-        o[db] = mfma32x32x16(va, pb[c], o[db]);
-      }
-    }
   }
 };
+
+// One step of attend_tiles: start the copy of tile kt+1 into `nxt` (when it
+// exists), consume tile kt from `cur`, then wait for the copy and sync.
+template <bool MASK, int NW>
+__device__ __forceinline__ void attend_step(WaveAttn& st, const TileLoader<NW>& ld,
+                                            const unsigned char* cur, unsigned char* nxt,
+                                            const uint16_t* kbase, const uint16_t* vbase,
+                                            int64_t sp, int kv0, bool more, int kend,
+                                            const u32x4 (&qb)[8], int lim_abs, int h2) {
+  // `nxt` was last read in the previous step, before its closing barrier
+  if (more) {
+    ld.load_k(kbase, sp, kv0 + kKeyTile, kend, nxt);
+    ld.load_v(vbase, sp, kv0 + kKeyTile, kend, nxt + kKTileBytes);
+  }
+  st.tile<MASK>(cur, qb, kv0, lim_abs, h2);
+  wait_tile_loads();
+  __syncthreads();
+}
+
+// Walk keys kbeg .. kend-1 in 64-key tiles with the NW waves of a workgroup.
+// Tile kt sits in stage kt & 1.  stage0 and stage1 must be two distinct
+// __shared__ arrays of kStageBytes: only then can the compiler see that the
+// reads of one stage do not depend on the copy in flight into the other (it
+// would otherwise wait for the copy before every read).  The first n_unmasked
+// tiles hold no key beyond any row's limit and run without mask code, two
+// per iteration so that each statically names its stage; the rest (the
+// diagonal) are masked: key kv0 + x counts only if kv0 + x <= lim_abs.
+// The caller issued the loads of the first tile into stage0 with
+// load_first().  Ends with a barrier.
+template <int NW>
+__device__ __forceinline__ void attend_tiles(WaveAttn& st, const TileLoader<NW>& ld,
+                                             unsigned char* stage0, unsigned char* stage1,
+                                             const uint16_t* kbase, const uint16_t* vbase,
+                                             int64_t sp, int kbeg, int kend, int n_unmasked,
+                                             const u32x4 (&qb)[8], int lim_abs, int h2) {
+  const int n_kt = (kend - kbeg + kKeyTile - 1) / kKeyTile;
+  wait_tile_loads();
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 2 <= n_unmasked; kt += 2) {
+    const int kv0 = kbeg + kt * kKeyTile;
+    attend_step<false>(st, ld, stage0, stage1, kbase, vbase, sp, kv0, true, kend, qb,
+                       lim_abs, h2);
+    attend_step<false>(st, ld, stage1, stage0, kbase, vbase, sp, kv0 + kKeyTile,
+                       kt + 2 < n_kt, kend, qb, lim_abs, h2);
+  }
+  for (; kt < n_kt; ++kt) {
+    const int kv0 = kbeg + kt * kKeyTile;
+    if ((kt & 1) == 0)
+      attend_step<true>(st, ld, stage0, stage1, kbase, vbase, sp, kv0, kt + 1 < n_kt,
+                        kend, qb, lim_abs, h2);
+    else
+      attend_step<true>(st, ld, stage1, stage0, kbase, vbase, sp, kv0, kt + 1 < n_kt,
+                        kend, qb, lim_abs, h2);
+  }
+}
+
+// First loads of attend_tiles: K and V of the tile at kbeg into stage0.
+template <int NW>
+__device__ __forceinline__ void load_first(const TileLoader<NW>& ld, unsigned char* stage0,
+                                           const uint16_t* kbase, const uint16_t* vbase,
+                                           int64_t sp, int kbeg, int kend) {
+  ld.load_k(kbase, sp, kbeg, kend, stage0);
+  ld.load_v(vbase, sp, kbeg, kend, stage0 + kKTileBytes);
+}
 
 // q' = RoPE(RMSNorm(q)) * qscale for the lane's half of one query row, packed
 // as the B operand of the QK product.  Lane half h2 owns dims

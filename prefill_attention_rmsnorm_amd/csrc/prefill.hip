@@ -67,7 +67,8 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(PrefillArgs a,
 template <int G>
 __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillArgs a) {
   constexpr int TQ = 128 / G;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStageBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char stage0[kStageBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char stage1[kStageBytes];
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int j = l & 31, h2 = l >> 5;
@@ -145,29 +146,20 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillArgs a) {
 
   const uint16_t* kbase = a.c.k + (size_t)seq * a.c.sb + (size_t)g * a.c.sh;
   const uint16_t* vbase = a.c.v + (size_t)seq * a.c.sb + (size_t)g * a.c.sh;
-  const int n_kt = (kv_end + kKeyTile - 1) / kKeyTile;
 
   TileLoader<4> ld;
   ld.init(__builtin_amdgcn_readfirstlane(w), l, a.c.sp);
-  ld.load(kbase, vbase, a.c.sp, 0, kv_end, smem);
+  load_first(ld, stage0, kbase, vbase, a.c.sp, 0, kv_end);
 
   u32x4 qb[8];
   qp.compute((float)a.eps, a.qscale, qb);
 
   WaveAttn st;
   st.init(l);
-  wait_tile_loads();
-  __syncthreads();
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int kv0 = kt * kKeyTile;
-    // the stage written here was last read in iteration kt-1, before the barrier
-    if (kt + 1 < n_kt)
-      ld.load(kbase, vbase, a.c.sp, kv0 + kKeyTile, kv_end,
-              smem + ((kt + 1) & 1) * kStageBytes);
-    st.tile(smem + (kt & 1) * kStageBytes, qb, kv0, kv0 + kKeyTile - 1 > pmin, p, h2);
-    wait_tile_loads();
-    __syncthreads();
-  }
+  // tiles wholly at or below the smallest position need no mask
+  const int n_unmasked = (pmin + 1) / kKeyTile;
+  attend_tiles(st, ld, stage0, stage1, kbase, vbase, a.c.sp, 0, kv_end, n_unmasked, qb,
+               p, h2);
 
   const float lt = st.lsum + __shfl_xor(st.lsum, 32);
   const float inv = q_ok ? 1.0f / lt : 0.f;

@@ -20,7 +20,9 @@ namespace qa {
 template <int G, int NW>
 __global__ __launch_bounds__(NW * 64) void verify_kernel(DecodeArgs a, RopeFreq f) {
   constexpr int NT = NW * 64;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStageBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char stage0[kStageBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char stage1[kStageBytes];
+  __shared__ __attribute__((aligned(16))) float2 cs[(128 / G) * kHalf];  // [draft token][pair]
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int j = l & 31, h2 = l >> 5;
@@ -62,7 +64,6 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(DecodeArgs a, RopeFreq 
 
     // ---- cos/sin of the draft positions for the queries (LDS, fp64
     // rotation recurrence from the block start, stored as fp32)
-    float2* cs = reinterpret_cast<float2*>(smem);  // [n][64], before staging
     if (w == 0) {
       double sb, cb, s1, c1;
       sincos((double)L0 * f.inv_freq[l], &sb, &cb);
@@ -87,26 +88,17 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(DecodeArgs a, RopeFreq 
 
     const uint16_t* kbase = a.c.k + (size_t)b * a.c.sb + (size_t)g * a.c.sh;
     const uint16_t* vbase = a.c.v + (size_t)b * a.c.sb + (size_t)g * a.c.sh;
-    const int n_kt = (k1 - k0 + kKeyTile - 1) / kKeyTile;
     TileLoader<NW> ld;
     ld.init(__builtin_amdgcn_readfirstlane(w), l, a.c.sp);
     WaveAttn st;
     st.init(l);
-    // the cs table in LDS is dead after the barrier above
-    ld.load(kbase, vbase, a.c.sp, k0, k1, smem);
-    wait_tile_loads();
-    __syncthreads();
+    load_first(ld, stage0, kbase, vbase, a.c.sp, k0, k1);
     const int lim_abs = row_ok ? min(p, k1 - 1) : k1 - 1;
-    for (int kt = 0; kt < n_kt; ++kt) {
-      const int kv0 = k0 + kt * kKeyTile;
-      if (kt + 1 < n_kt)
-        ld.load(kbase, vbase, a.c.sp, kv0 + kKeyTile, k1,
-                smem + ((kt + 1) & 1) * kStageBytes);
-      const bool need_mask = (kv0 + kKeyTile > k1) || (kv0 + kKeyTile - 1 > L0);
-      st.tile(smem + (kt & 1) * kStageBytes, qb, kv0, need_mask, lim_abs, h2);
-      wait_tile_loads();
-      __syncthreads();
-    }
+    // tiles whose keys all lie below k1 and at or below the first draft
+    // position need no mask
+    const int n_unmasked = max(min(k1 - 1, L0) + 1 - k0, 0) / kKeyTile;
+    attend_tiles(st, ld, stage0, stage1, kbase, vbase, a.c.sp, k0, k1, n_unmasked, qb,
+                 lim_abs, h2);
     if (row_ok) {
       const float lt = st.lsum + __shfl_xor(st.lsum, 32);
       if (h2 == 0) {
