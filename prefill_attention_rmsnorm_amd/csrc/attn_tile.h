@@ -25,9 +25,6 @@ namespace qa {
 
 constexpr int kRowBytes = kHeadDim * 2;                   // 256
 constexpr int kKTileBytes = kKeyTile * kRowBytes;         // 16384
-// One LDS stage holds a K tile and then a V tile.
-constexpr int kStageBytes = 2 * kKTileBytes;
-constexpr float kRescaleSlack = 8.0f;  // log2 units a stale max may lag by
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -108,21 +105,48 @@ __device__ __forceinline__ void wait_tile_loads() {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 }
 
+// The four LDS tiles of a workgroup: K and V, double-buffered.  They must be
+// four distinct __shared__ arrays of kKTileBytes: only then can the compiler
+// see that reads of one buffer do not depend on a copy in flight into
+// another (it would otherwise wait for the copy before every read).
+struct AttnLds {
+  unsigned char* k0;
+  unsigned char* k1;
+  unsigned char* v0;
+  unsigned char* v1;
+};
+
+// Scores above the block's reference max by more than this (log2 units), or
+// an output that large, send the block to the exact-max path.
+constexpr float kSumLimit = 0x1p96f;
+constexpr float kOutLimit = 0x1p126f;
+
 // Per-wave attention state for 32 query columns.
+//
+// Softmax with a reference max fixed per workgroup: m is the row max over
+// the first tile processed, and every later tile uses p = exp2(s - m) with
+// no rescaling of O.  Softmax is invariant to the shift, so this is the same
+// quantity as with the running max as long as nothing overflows; a later
+// score far above m shows up as a huge row sum, and the caller then redoes
+// the block with the exact row max (where p <= 1 everywhere).
 struct WaveAttn {
   f32x16 o[4];  // O^T, d-block db: rows d = 32*db + 8*(r/4) + 4*h2 + r%4
-  float m;      // running (possibly stale) max, log2 domain, per query
+  float m;      // reference max (log2 domain), per query
   float lsum;   // sum of this lane's half of the bf16-rounded probabilities
   uint32_t kb;  // LDS byte offset of this lane's K operand at k-step 0
   uint32_t vb;  // LDS byte offset of this lane's V^T piece at d-block 0
 
-  __device__ __forceinline__ void init(int lane) {
+  __device__ __forceinline__ void reset() {
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-    m = -__builtin_inff();
     lsum = 0.f;
+  }
+
+  __device__ __forceinline__ void init(int lane) {
+    reset();
+    m = 0.f;
     const int j = lane & 31, h2 = lane >> 5;
     // K operand: row sigma(j) (+32 for the second 32-key block), dims
     // 16*kstep + 8*h2 .. +7 = logical chunk 2*kstep + h2, stored at chunk
@@ -140,118 +164,93 @@ struct WaveAttn {
     vb = (uint32_t)((8 * (g16 >> 1) + e) * kRowBytes + 64 * e + 16 * x + 8 * (r4 & 1));
   }
 
-  // One 64-key tile in LDS: K at stage, V at stage + kKTileBytes.
-  // All K operand reads are issued before the QK MFMAs and all V^T reads
-  // before the softmax, so LDS latency is paid about once per phase.
-  // With MASK, key kv0 + x counts only if kv0 + x <= lim_abs, where
-  // lim_abs = min(query position, last valid key).  (A separate instantiation
-  // keeps the unmasked scores straight from the MFMA, which lets the max run
-  // as v_max3 without quieting every input first.)
-  template <bool MASK>
-  __device__ __forceinline__ void tile(const unsigned char* stage,
-                                       const u32x4 (&qb)[8], int kv0,
-                                       int lim_abs, int h2) {
-    // Re-derive the per-k-step and per-d-block LDS offsets inside each tile
-    // (one XOR each) instead of keeping a dozen of them live across the loop.
-    uint32_t kbt = kb, vbt = vb;
+  // K operand of one k-step for keys 0-31 (a0) and 32-63 (a1).
+  __device__ __forceinline__ static void read_k(const unsigned char* kt, uint32_t kbt,
+                                                int kstep, u32x4& a0, u32x4& a1) {
+    const uint32_t off = kbt ^ (32u * kstep);
+    a0 = *reinterpret_cast<const u32x4*>(kt + off);
+    a1 = *reinterpret_cast<const u32x4*>(kt + off + 32 * kRowBytes);
+  }
+
+  // V^T operand of d-block db, 16-key chunk c (two transposing reads of 4
+  // keys each, landing in the two halves of one operand).
+  __device__ __forceinline__ static u32x4 read_vt(const unsigned char* vt, uint32_t vbt,
+                                                  int db, int c) {
+    const uint32_t vo = vbt ^ (64u * db);
+    const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(vt + vo + 16 * c * kRowBytes));
+    const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(vt + vo + (16 * c + 4) * kRowBytes));
+    return __builtin_bit_cast(u32x4, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+
+  // Re-derive the LDS offsets in each tile (one XOR per use) rather than
+  // keeping a dozen of them live across the loop.
+  __device__ __forceinline__ void offsets(uint32_t& kbt, uint32_t& vbt) const {
+    kbt = kb;
+    vbt = vb;
     asm volatile("" : "+v"(kbt), "+v"(vbt));
-    // K operands in a ring of 4 k-steps: reads run two k-steps ahead of use
-    u32x4 ka[8];
-    read_k(stage, kbt, 0, ka[0], ka[1]);
-    read_k(stage, kbt, 1, ka[2], ka[3]);
-    read_k(stage, kbt, 2, ka[4], ka[5]);
-    read_k(stage, kbt, 3, ka[6], ka[7]);
-    __builtin_amdgcn_sched_barrier(0);
-    f32x16 s0, s1;
+  }
+
+  // S^T of the 64 keys of the K tile kt: s0 keys 0-31, s1 keys 32-63;
+  // register r of lane half h2 holds key 16*(r/8) + 8*h2 + r%8 (+32 in s1).
+  __device__ __forceinline__ static void qk(const unsigned char* kt, uint32_t kbt,
+                                            const u32x4 (&qb)[8], f32x16& s0, f32x16& s1) {
+    u32x4 ka[8];  // ring of 4 k-steps, reads two k-steps ahead of use
+    read_k(kt, kbt, 0, ka[0], ka[1]);
+    read_k(kt, kbt, 1, ka[2], ka[3]);
+    read_k(kt, kbt, 2, ka[4], ka[5]);
+    read_k(kt, kbt, 3, ka[6], ka[7]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
 #pragma unroll
     for (int kstep = 0; kstep < 8; kstep += 2) {
-      const int u = (kstep & 3) * 2;  // ring slot of this k-step pair
+      const int u = (kstep & 3) * 2;
       s0 = mfma32x32x16(ka[u], qb[kstep], s0);
       s1 = mfma32x32x16(ka[u + 1], qb[kstep], s1);
       s0 = mfma32x32x16(ka[u + 2], qb[kstep + 1], s0);
       s1 = mfma32x32x16(ka[u + 3], qb[kstep + 1], s1);
       if (kstep + 4 < 8) {
-        read_k(stage, kbt, kstep + 4, ka[u], ka[u + 1]);
-        read_k(stage, kbt, kstep + 5, ka[u + 2], ka[u + 3]);
+        read_k(kt, kbt, kstep + 4, ka[u], ka[u + 1]);
+        read_k(kt, kbt, kstep + 5, ka[u + 2], ka[u + 3]);
       }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    u32x4 va[16];  // [db][c]; d-blocks 0-1 before the softmax, 2-3 after
-    read_vt(stage, vbt, 0, va);
-    read_vt(stage, vbt, 1, va);
-    __builtin_amdgcn_sched_barrier(0);
-    u32x4 pb[4];
-    softmax<MASK>(s0, s1, kv0, lim_abs, h2, pb);
-    __builtin_amdgcn_sched_barrier(0);
-    read_vt(stage, vbt, 2, va);
-    read_vt(stage, vbt, 3, va);
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) o[db] = mfma32x32x16(va[4 * db + c], pb[c], o[db]);
-  }
-
-  // K operand of one k-step for keys 0-31 (a0) and 32-63 (a1).
-  __device__ __forceinline__ static void read_k(const unsigned char* stage, uint32_t kbt,
-                                                int kstep, u32x4& a0, u32x4& a1) {
-    const uint32_t off = kbt ^ (32u * kstep);
-    a0 = *reinterpret_cast<const u32x4*>(stage + off);
-    a1 = *reinterpret_cast<const u32x4*>(stage + off + 32 * kRowBytes);
-  }
-
-  // V^T operand of d-block db for the four 16-key chunks (two transposing
-  // reads of 4 keys each per chunk, landing in the two halves of one operand).
-  __device__ __forceinline__ static void read_vt(const unsigned char* stage, uint32_t vbt,
-                                                 int db, u32x4 (&va)[16]) {
-    const uint32_t vo = kKTileBytes + (vbt ^ (64u * db));
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)(stage + vo + 16 * c * kRowBytes));
-      const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)(stage + vo + (16 * c + 4) * kRowBytes));
-      va[4 * db + c] = __builtin_bit_cast(u32x4, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
     }
   }
 
-  // Online softmax of one tile's scores into bf16 P^T (pb[c]: keys 16c..16c+15).
-  template <bool MASK>
-  __device__ __forceinline__ void softmax(f32x16& s0, f32x16& s1, int kv0,
-                                          int lim_abs, int h2, u32x4 (&pb)[4]) {
+  // Masks keys kv0 + x > lim_abs (lim_abs = min(query position, last valid
+  // key)) to -inf.
+  __device__ __forceinline__ static void mask(f32x16& s0, f32x16& s1, int kv0,
+                                              int lim_abs, int h2) {
     const float ninf = -__builtin_inff();
-    if (MASK) {
-      const int lim = lim_abs - kv0 - 8 * h2;
+    const int lim = lim_abs - kv0 - 8 * h2;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kr = 16 * (r >> 3) + (r & 7);
-        s0[r] = (kr > lim) ? ninf : s0[r];
-        s1[r] = (kr + 32 > lim) ? ninf : s1[r];
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int kr = 16 * (r >> 3) + (r & 7);
+      s0[r] = (kr > lim) ? ninf : s0[r];
+      s1[r] = (kr + 32 > lim) ? ninf : s1[r];
     }
-    // v_max3 straight on the scores (fmaxf would first quiet every input)
-    float mt = ninf;
+  }
+
+  // Row max of a tile's (masked) scores, both lane halves combined.
+  __device__ __forceinline__ static float row_max(const f32x16& s0, const f32x16& s1) {
+    float mt = -__builtin_inff();
 #pragma unroll
     for (int r = 0; r < 16; ++r) mt = max3_f32(mt, s0[r], s1[r]);
-    // The max is refreshed only when a score passes the stale one by more
-    // than kRescaleSlack, so p <= 2^kRescaleSlack and the O rescale is rare.
-    if (__any(mt > m + kRescaleSlack)) {
-      const float mn = fmaxf(m, fmaxf(mt, __shfl_xor(mt, 32)));
-      // a row with no visible key so far keeps m = -inf (o and lsum are 0)
-      const float alpha = (mn == ninf) ? 1.f : __builtin_amdgcn_exp2f(m - mn);
-#pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] = o[db] * alpha;
-      lsum *= alpha;
-      m = mn;
-    }
-    const float mu = (m == ninf) ? 0.f : m;
+    return fmaxf(mt, __shfl_xor(mt, 32));
+  }
+
+  // Scores -> bf16 P^T (pb[c]: keys 16c .. 16c+15) with the reference max;
+  // the row sum accumulates the rounded values.
+  template <bool MASK>
+  __device__ __forceinline__ void probs(f32x16& s0, f32x16& s1, int kv0, int lim_abs,
+                                        int h2, u32x4 (&pb)[4]) {
+    if (MASK) mask(s0, s1, kv0, lim_abs, h2);
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      pb[r >> 3][(r & 7) >> 1] = pack_bf16x2(__builtin_amdgcn_exp2f(s0[r] - mu),
-                                             __builtin_amdgcn_exp2f(s0[r + 1] - mu));
-      pb[2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(__builtin_amdgcn_exp2f(s1[r] - mu),
-                                                   __builtin_amdgcn_exp2f(s1[r + 1] - mu));
+      pb[r >> 3][(r & 7) >> 1] = pack_bf16x2(__builtin_amdgcn_exp2f(s0[r] - m),
+                                             __builtin_amdgcn_exp2f(s0[r + 1] - m));
+      pb[2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(__builtin_amdgcn_exp2f(s1[r] - m),
+                                                   __builtin_amdgcn_exp2f(s1[r + 1] - m));
     }
     constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 (1, 1)
 #pragma unroll
@@ -259,71 +258,226 @@ struct WaveAttn {
 #pragma unroll
       for (int i = 0; i < 4; ++i) lsum = dot2_bf16(pb[c][i], kOnes, lsum);
   }
+
+  // QK of the next tile (K tile kn, into sn) interleaved with the
+  // probabilities of the current tile (sc -> pb): the MFMAs run while the
+  // VALU computes exponentials.
+  template <bool MASK>
+  __device__ __forceinline__ void qk_probs(const unsigned char* kn, uint32_t kbt,
+                                           const u32x4 (&qb)[8], f32x16& sn0, f32x16& sn1,
+                                           f32x16& sc0, f32x16& sc1, int kv0, int lim_abs,
+                                           int h2, u32x4 (&pb)[4]) {
+    qk(kn, kbt, qb, sn0, sn1);
+    probs<MASK>(sc0, sc1, kv0, lim_abs, h2, pb);
+    // 16 MFMAs, 16 LDS reads and ~100 VALU: one MFMA, one read, six VALU
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
+  }
+
+  // O^T += V^T . P^T with the V tile vt.
+  __device__ __forceinline__ void pv(const unsigned char* vt, uint32_t vbt,
+                                     const u32x4 (&pb)[4]) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      u32x4 va[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) va[c] = read_vt(vt, vbt, db, c);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[db] = mfma32x32x16(va[c], pb[c], o[db]);
+    }
+  }
+
+  // P.V of one tile (V tile vt, probabilities pb) followed by the QK product
+  // of the next K tile kn into s0/s1, with LDS reads issued two groups of
+  // MFMAs ahead: for a wave that is alone on the matrix core, nothing else
+  // hides the read latency.
+  template <bool QK>
+  __device__ __forceinline__ void pv_qk(const unsigned char* vt, uint32_t vbt,
+                                        const u32x4 (&pb)[4], const unsigned char* kn,
+                                        uint32_t kbt, const u32x4 (&qb)[8], f32x16& s0,
+                                        f32x16& s1) {
+    u32x4 va[8], ka[8];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) va[c] = read_vt(vt, vbt, 0, c);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) va[4 + c] = read_vt(vt, vbt, 1, c);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int u = (db & 1) * 4;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[db] = mfma32x32x16(va[u + c], pb[c], o[db]);
+      if (db + 2 < 4) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) va[u + c] = read_vt(vt, vbt, db + 2, c);
+      } else if (QK) {
+        read_k(kn, kbt, 2 * (db - 2), ka[4 * (db - 2)], ka[4 * (db - 2) + 1]);
+        read_k(kn, kbt, 2 * (db - 2) + 1, ka[4 * (db - 2) + 2], ka[4 * (db - 2) + 3]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (!QK) return;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
+#pragma unroll
+    for (int kstep = 0; kstep < 8; kstep += 2) {
+      const int u = (kstep & 3) * 2;
+      s0 = mfma32x32x16(ka[u], qb[kstep], s0);
+      s1 = mfma32x32x16(ka[u + 1], qb[kstep], s1);
+      s0 = mfma32x32x16(ka[u + 2], qb[kstep + 1], s0);
+      s1 = mfma32x32x16(ka[u + 3], qb[kstep + 1], s1);
+      if (kstep + 4 < 8) {
+        read_k(kn, kbt, kstep + 4, ka[u], ka[u + 1]);
+        read_k(kn, kbt, kstep + 5, ka[u + 2], ka[u + 3]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // Whether this lane's results might have overflowed the reference max
+  // (row sum or |O| too large, or not finite).
+  __device__ __forceinline__ bool overflowed() const {
+    const float lt = lsum + __shfl_xor(lsum, 32);
+    float om = 0.f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) om = fmaxf(om, fabsf(o[db][r]));
+    return !(lt < kSumLimit) || !(om < kOutLimit);
+  }
 };
 
-// One step of attend_tiles: start the copy of tile kt+1 into `nxt` (when it
-// exists), consume tile kt from `cur`, then wait for the copy and sync.
-template <bool MASK, int NW>
-__device__ __forceinline__ void attend_step(WaveAttn& st, const TileLoader<NW>& ld,
-                                            const unsigned char* cur, unsigned char* nxt,
-                                            const uint16_t* kbase, const uint16_t* vbase,
-                                            int64_t sp, int kv0, bool more, int kend,
-                                            const u32x4 (&qb)[8], int lim_abs, int h2) {
-  // `nxt` was last read in the previous step, before its closing barrier
-  if (more) {
-    ld.load_k(kbase, sp, kv0 + kKeyTile, kend, nxt);
-    ld.load_v(vbase, sp, kv0 + kKeyTile, kend, nxt + kKTileBytes);
-  }
-  st.tile<MASK>(cur, qb, kv0, lim_abs, h2);
-  wait_tile_loads();
-  __syncthreads();
-}
-
-// Walk keys kbeg .. kend-1 in 64-key tiles with the NW waves of a workgroup.
-// Tile kt sits in stage kt & 1.  stage0 and stage1 must be two distinct
-// __shared__ arrays of kStageBytes: only then can the compiler see that the
-// reads of one stage do not depend on the copy in flight into the other (it
-// would otherwise wait for the copy before every read).  The first n_unmasked
-// tiles hold no key beyond any row's limit and run without mask code, two
-// per iteration so that each statically names its stage; the rest (the
-// diagonal) are masked: key kv0 + x counts only if kv0 + x <= lim_abs.
-// The caller issued the loads of the first tile into stage0 with
-// load_first().  Ends with a barrier.
+// First loads of attend_pass: K and V of the tile at kbeg, K of the next.
 template <int NW>
-__device__ __forceinline__ void attend_tiles(WaveAttn& st, const TileLoader<NW>& ld,
-                                             unsigned char* stage0, unsigned char* stage1,
-                                             const uint16_t* kbase, const uint16_t* vbase,
-                                             int64_t sp, int kbeg, int kend, int n_unmasked,
-                                             const u32x4 (&qb)[8], int lim_abs, int h2) {
-  const int n_kt = (kend - kbeg + kKeyTile - 1) / kKeyTile;
-  wait_tile_loads();
-  __syncthreads();
-  int kt = 0;
-  for (; kt + 2 <= n_unmasked; kt += 2) {
-    const int kv0 = kbeg + kt * kKeyTile;
-    attend_step<false>(st, ld, stage0, stage1, kbase, vbase, sp, kv0, true, kend, qb,
-                       lim_abs, h2);
-    attend_step<false>(st, ld, stage1, stage0, kbase, vbase, sp, kv0 + kKeyTile,
-                       kt + 2 < n_kt, kend, qb, lim_abs, h2);
-  }
-  for (; kt < n_kt; ++kt) {
-    const int kv0 = kbeg + kt * kKeyTile;
-    if ((kt & 1) == 0)
-      attend_step<true>(st, ld, stage0, stage1, kbase, vbase, sp, kv0, kt + 1 < n_kt,
-                        kend, qb, lim_abs, h2);
-    else
-      attend_step<true>(st, ld, stage1, stage0, kbase, vbase, sp, kv0, kt + 1 < n_kt,
-                        kend, qb, lim_abs, h2);
-  }
-}
-
-// First loads of attend_tiles: K and V of the tile at kbeg into stage0.
-template <int NW>
-__device__ __forceinline__ void load_first(const TileLoader<NW>& ld, unsigned char* stage0,
+__device__ __forceinline__ void load_first(const TileLoader<NW>& ld, const AttnLds& lds,
                                            const uint16_t* kbase, const uint16_t* vbase,
                                            int64_t sp, int kbeg, int kend) {
-  ld.load_k(kbase, sp, kbeg, kend, stage0);
-  ld.load_v(vbase, sp, kbeg, kend, stage0 + kKTileBytes);
+  ld.load_k(kbase, sp, kbeg, kend, lds.k0);
+  ld.load_v(vbase, sp, kbeg, kend, lds.v0);
+  if (kbeg + kKeyTile < kend) ld.load_k(kbase, sp, kbeg + kKeyTile, kend, lds.k1);
+}
+
+// One pass over keys kbeg .. kend-1 in 64-key tiles.  Tile kt's K sits in
+// k(kt&1) and its V in v(kt&1); while tile kt is consumed, K of tile kt+2
+// and V of tile kt+1 load, and the QK product of tile kt+1 runs interleaved
+// with the exponentials of tile kt.  The first n_unmasked tiles hold no key
+// beyond any row's limit; the rest (the diagonal) are masked: key kv0 + x
+// counts only if kv0 + x <= lim_abs.  With SET_M the reference max is taken
+// from the first tile, otherwise st.m is used as given.  The caller issued
+// load_first().  Ends with a barrier.
+template <bool SET_M, int NW>
+__device__ __forceinline__ void attend_pass(WaveAttn& st, const TileLoader<NW>& ld,
+                                            const AttnLds& lds, const uint16_t* kbase,
+                                            const uint16_t* vbase, int64_t sp, int kbeg,
+                                            int kend, int n_unmasked, const u32x4 (&qb)[8],
+                                            int lim_abs, int h2) {
+  const int n_kt = (kend - kbeg + kKeyTile - 1) / kKeyTile;
+  uint32_t kbt, vbt;
+  st.offsets(kbt, vbt);
+  wait_tile_loads();
+  __syncthreads();
+  f32x16 sc0, sc1, sn0, sn1;
+  WaveAttn::qk(lds.k0, kbt, qb, sc0, sc1);
+  if (SET_M) {
+    f32x16 t0 = sc0, t1 = sc1;
+    if (n_unmasked == 0) WaveAttn::mask(t0, t1, kbeg, lim_abs, h2);
+    st.m = WaveAttn::row_max(t0, t1);
+  }
+  __syncthreads();  // every wave has read K tile 0 before it is reloaded
+  int kt = 0;
+  // steady state: two unmasked tiles per iteration, each naming its buffers
+  for (; kt + 2 < n_kt && kt + 2 <= n_unmasked; kt += 2) {
+    const int kv0 = kbeg + kt * kKeyTile;
+    u32x4 pb[4];
+    ld.load_k(kbase, sp, kv0 + 2 * kKeyTile, kend, lds.k0);
+    ld.load_v(vbase, sp, kv0 + kKeyTile, kend, lds.v1);
+    st.qk_probs<false>(lds.k1, kbt, qb, sn0, sn1, sc0, sc1, kv0, lim_abs, h2, pb);
+    st.pv(lds.v0, vbt, pb);
+    sc0 = sn0;
+    sc1 = sn1;
+    wait_tile_loads();
+    __syncthreads();
+    if (kt + 3 < n_kt) ld.load_k(kbase, sp, kv0 + 3 * kKeyTile, kend, lds.k1);
+    ld.load_v(vbase, sp, kv0 + 2 * kKeyTile, kend, lds.v0);
+    st.qk_probs<false>(lds.k0, kbt, qb, sn0, sn1, sc0, sc1, kv0 + kKeyTile, lim_abs, h2, pb);
+    st.pv(lds.v1, vbt, pb);
+    sc0 = sn0;
+    sc1 = sn1;
+    wait_tile_loads();
+    __syncthreads();
+  }
+  // the rest (the diagonal; usually one or two tiles), masked, one tile per
+  // iteration and not interleaved: probabilities, PV, then QK of the next
+  // tile into the same score registers
+  const unsigned char* knext = (kt & 1) ? lds.k0 : lds.k1;  // K of tile kt+1
+  unsigned char* kload = (kt & 1) ? lds.k1 : lds.k0;        // for K of tile kt+2
+  const unsigned char* vcur = (kt & 1) ? lds.v1 : lds.v0;   // V of tile kt
+  unsigned char* vload = (kt & 1) ? lds.v0 : lds.v1;        // for V of tile kt+1
+  for (; kt < n_kt; ++kt) {
+    const int kv0 = kbeg + kt * kKeyTile;
+    if (kt + 2 < n_kt) ld.load_k(kbase, sp, kv0 + 2 * kKeyTile, kend, kload);
+    if (kt + 1 < n_kt) ld.load_v(vbase, sp, kv0 + kKeyTile, kend, vload);
+    u32x4 pb[4];
+    st.probs<true>(sc0, sc1, kv0, lim_abs, h2, pb);
+    st.pv(vcur, vbt, pb);
+    if (kt + 1 < n_kt) WaveAttn::qk(knext, kbt, qb, sc0, sc1);
+    wait_tile_loads();
+    __syncthreads();
+    const unsigned char* kt_ = knext;
+    knext = kload;
+    kload = const_cast<unsigned char*>(kt_);
+    const unsigned char* vt_ = vcur;
+    vcur = vload;
+    vload = const_cast<unsigned char*>(vt_);
+  }
+}
+
+// Exact row max over keys kbeg .. kend-1 (QK only, K tiles double-buffered).
+template <int NW>
+__device__ __forceinline__ float exact_row_max(const WaveAttn& st, const TileLoader<NW>& ld,
+                                               const AttnLds& lds, const uint16_t* kbase,
+                                               int64_t sp, int kbeg, int kend,
+                                               const u32x4 (&qb)[8], int lim_abs, int h2) {
+  const int n_kt = (kend - kbeg + kKeyTile - 1) / kKeyTile;
+  uint32_t kbt, vbt;
+  st.offsets(kbt, vbt);
+  float mx = -__builtin_inff();
+  ld.load_k(kbase, sp, kbeg, kend, lds.k0);
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int kv0 = kbeg + kt * kKeyTile;
+    wait_tile_loads();
+    __syncthreads();
+    const unsigned char* cur = (kt & 1) ? lds.k1 : lds.k0;
+    if (kt + 1 < n_kt) ld.load_k(kbase, sp, kv0 + kKeyTile, kend, (kt & 1) ? lds.k0 : lds.k1);
+    f32x16 s0, s1;
+    WaveAttn::qk(cur, kbt, qb, s0, s1);
+    WaveAttn::mask(s0, s1, kv0, lim_abs, h2);
+    mx = fmaxf(mx, WaveAttn::row_max(s0, s1));
+    __syncthreads();  // reads of `cur` done before it is reloaded
+  }
+  return mx;
+}
+
+// Attention of this wave's 32 query rows over keys kbeg .. kend-1 (see
+// attend_pass), with the exact-max fallback.  The caller issued load_first().
+template <int NW>
+__device__ __forceinline__ void attend(WaveAttn& st, const TileLoader<NW>& ld,
+                                       const AttnLds& lds, const uint16_t* kbase,
+                                       const uint16_t* vbase, int64_t sp, int kbeg, int kend,
+                                       int n_unmasked, const u32x4 (&qb)[8], int lim_abs,
+                                       int h2) {
+  attend_pass<true>(st, ld, lds, kbase, vbase, sp, kbeg, kend, n_unmasked, qb, lim_abs, h2);
+  if (__syncthreads_or(st.overflowed())) {
+    st.m = exact_row_max(st, ld, lds, kbase, sp, kbeg, kend, qb, lim_abs, h2);
+    st.reset();
+    load_first(ld, lds, kbase, vbase, sp, kbeg, kend);
+    attend_pass<false>(st, ld, lds, kbase, vbase, sp, kbeg, kend, n_unmasked, qb, lim_abs,
+                       h2);
+  }
 }
 
 // q' = RoPE(RMSNorm(q)) * qscale for the lane's half of one query row, packed

@@ -14,19 +14,28 @@
 namespace qa {
 
 // One wave per token: cos/sin of its angles, then k' and v of every KV head.
+// Eight lanes per KV head and eight heads at a time: lane group gh (lanes
+// 8gh .. 8gh+7) holds head gh, lane sub = lane & 7 its rotation pairs
+// i = 8*sub + e (e < 8), i.e. dims 8*sub .. +7 and 64 + 8*sub .. +7, read as
+// two 16-byte pieces.  The head's sum of squares is then a 3-step reduction
+// inside the group (exact in fp64 for bf16 inputs of moderate range, so its
+// order does not matter), and the arithmetic per element is the fp64
+// sequence x / r * w, rotation, one round to bf16.
 __global__ __launch_bounds__(256) void kv_prologue_kernel(PrefillArgs a,
                                                           RopeFreq f) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  __shared__ double2 s_cs[4][kHalf];  // per wave: (cos, sin) of the 64 pairs
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wv;
   if (t >= a.total_tokens) return;
   const int pos = a.positions[t];
 
-  double sn = 0.0, cn = 1.0;
   {
+    double sn = 0.0, cn = 1.0;
     const double ang = (double)pos * f.inv_freq[lane];
     sincos(ang, &sn, &cn);
+    a.cs[(size_t)t * kHalf + lane] = make_float2((float)cn, (float)sn);
+    s_cs[wv][lane] = make_double2(cn, sn);
   }
-  a.cs[(size_t)t * kHalf + lane] = make_float2((float)cn, (float)sn);
 
   // sequence owning token t: the last i with cu[i] <= t
   int lo = 0, hi = a.n_seq;
@@ -43,34 +52,225 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(PrefillArgs a,
     if (lane == 0) flag_error(a.err, QA_DEVERR_POSITION);
     return;
   }
-  const double w_lo = a.k_norm_w ? (double)bf_to_f(a.k_norm_w[lane]) : 1.0;
-  const double w_hi = a.k_norm_w ? (double)bf_to_f(a.k_norm_w[lane + 64]) : 1.0;
+  const int gh = lane >> 3, sub = lane & 7;
+  double w0[8], w1[8];
+  {
+    u32x4 wa = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u}, wb = wa;
+    if (a.k_norm_w) {
+      wa = ld16(a.k_norm_w + 8 * sub);
+      wb = ld16(a.k_norm_w + 64 + 8 * sub);
+    }
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      w0[2 * e2] = bf_lo(wa[e2]); w0[2 * e2 + 1] = bf_hi(wa[e2]);
+      w1[2 * e2] = bf_lo(wb[e2]); w1[2 * e2 + 1] = bf_hi(wb[e2]);
+    }
+  }
+  __builtin_amdgcn_wave_barrier();  // s_cs of this wave written
+  double cs_c[8], cs_s[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const double2 v = s_cs[wv][8 * sub + e];
+    cs_c[e] = v.x;
+    cs_s[e] = v.y;
+  }
   const size_t row0 = (size_t)lo * a.c.sb + (size_t)pos * a.c.sp;
-  for (int g = 0; g < a.n_kv_heads; ++g) {
-    const uint16_t* kr = a.k + (size_t)t * a.kv_tok_stride + (size_t)g * kHeadDim;
-    uint16_t o0, o1;
-    kprime_pair(kr[lane], kr[lane + 64], w_lo, w_hi, a.eps, cn, sn, &o0, &o1);
-    uint16_t* ck = a.c.k + row0 + (size_t)g * a.c.sh;
-    ck[lane] = o0;
-    ck[lane + 64] = o1;
-    const uint32_t* vr = reinterpret_cast<const uint32_t*>(
-        a.v + (size_t)t * a.kv_tok_stride + (size_t)g * kHeadDim);
-    reinterpret_cast<uint32_t*>(a.c.v + row0 + (size_t)g * a.c.sh)[lane] = vr[lane];
+  for (int g0 = 0; g0 < a.n_kv_heads; g0 += 8) {
+    const int g = g0 + gh;
+    const bool active = g < a.n_kv_heads;  // a whole lane group at once
+    const size_t src = (size_t)t * a.kv_tok_stride + (size_t)(active ? g : 0) * kHeadDim;
+    const u32x4 ka = ld16(a.k + src + 8 * sub), kb = ld16(a.k + src + 64 + 8 * sub);
+    const u32x4 va = ld16(a.v + src + 8 * sub), vb = ld16(a.v + src + 64 + 8 * sub);
+    double x0[8], x1[8];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      x0[2 * e2] = bf_lo(ka[e2]); x0[2 * e2 + 1] = bf_hi(ka[e2]);
+      x1[2 * e2] = bf_lo(kb[e2]); x1[2 * e2 + 1] = bf_hi(kb[e2]);
+    }
+    u32x4 oa, ob;
+    {
+#pragma clang fp contract(off)
+      double ss = 0.0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += x0[e] * x0[e] + x1[e] * x1[e];
+      ss += __shfl_xor(ss, 1);
+      ss += __shfl_xor(ss, 2);
+      ss += __shfl_xor(ss, 4);
+      const double r = sqrt(ss / 128.0 + a.eps);
+      uint16_t o0[8], o1[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const double y0 = x0[e] / r * w0[e];
+        const double y1 = x1[e] / r * w1[e];
+        o0[e] = f64_to_bf16_rne(y0 * cs_c[e] - y1 * cs_s[e]);
+        o1[e] = f64_to_bf16_rne(y1 * cs_c[e] + y0 * cs_s[e]);
+      }
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        oa[e2] = (uint32_t)o0[2 * e2] | ((uint32_t)o0[2 * e2 + 1] << 16);
+        ob[e2] = (uint32_t)o1[2 * e2] | ((uint32_t)o1[2 * e2 + 1] << 16);
+      }
+    }
+    if (active) {
+      uint16_t* ck = a.c.k + row0 + (size_t)g * a.c.sh;
+      uint16_t* cv = a.c.v + row0 + (size_t)g * a.c.sh;
+      st16(ck + 8 * sub, oa);
+      st16(ck + 64 + 8 * sub, ob);
+      st16(cv + 8 * sub, va);
+      st16(cv + 64 + 8 * sub, vb);
+    }
   }
 }
 
-// Workgroup = 4 waves = 128 query rows = G heads x (128/G) tokens of one
-// sequence and KV head.  Blocks are ordered heaviest q-tile first; when the
-// number of (sequence, kv head) pairs is a multiple of 8, all tiles of a pair
-// land on one XCD (the hardware deals workgroup ids to the 8 XCDs round
-// robin), so its K/V stay in that XCD's L2.
-template <int G>
-__global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillArgs a) {
-  constexpr int TQ = 128 / G;
-  __shared__ __attribute__((aligned(16))) unsigned char stage0[kStageBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char stage1[kStageBytes];
+// ---------------------------------------------------------------------------
+// Attention: workgroup = 8 waves = 256 query rows = G heads x (256/G) tokens
+// of one sequence and KV head, all sharing every K/V tile.  Waves 0-3 (group
+// A) and 4-7 (group B) sit one of each on every SIMD and run the same tile
+// sequence half a tile apart: each tile takes two barrier-separated phases,
+// and in every phase one group issues the MFMA work (P.V of the previous
+// tile, then Q.K of the next) while the other group computes the
+// exponentials of its current scores.  The matrix core thus always has a
+// wave feeding it while the softmax runs on the vector ALUs.
+//
+// Phase 2k (even) starts the copies of K tile k+1 and V tile k (into the
+// buffers whose previous contents were last read two phases earlier); phase
+// 2k+1 (odd) ends with every wave waiting for its copies.  Only group B
+// issues copies: its even phases are its exponential phases, which have
+// slack, while a copy issued by the MFMA group delays its first MFMA.  Group A runs
+// M(k) in phase 2k and V(k) in 2k+1; group B one phase later; both pass
+// the same number of barriers.
+//   M(k): O += V(k-1)^T . P(k-1)^T (k >= 1);  S = K(k) . Q'^T (k < n_kt)
+//   V(k): P(k) = exp2(S - m) as bf16, masked on the diagonal tiles
 
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+template <int PAR>
+__device__ __forceinline__ void pp_loads(const TileLoader<4>& ld, const AttnLds& lds,
+                                         const uint16_t* kbase, const uint16_t* vbase,
+                                         int64_t sp, int kend, int kk, int n_kt) {
+  // even phase 2kk: K(kk+1) -> k[(kk+1)&1], V(kk) -> v[kk&1]; PAR = kk & 1
+  if (kk + 1 < n_kt) ld.load_k(kbase, sp, (kk + 1) * kKeyTile, kend, PAR ? lds.k0 : lds.k1);
+  if (kk < n_kt) ld.load_v(vbase, sp, kk * kKeyTile, kend, PAR ? lds.v1 : lds.v0);
+}
+
+// Keep a phase's results on its own side of the barrier that ends it: the
+// barrier orders memory only, and the compiler would otherwise sink pure
+// ALU work (the exponentials, or MFMAs) into the next phase, where it would
+// serialise with the other kind of work instead of overlapping the other
+// group's.
+__device__ __forceinline__ void pin(const u32x4 (&pb)[4], float x) {
+  asm volatile("" ::"v"(pb[0]), "v"(pb[1]), "v"(pb[2]), "v"(pb[3]), "v"(x));
+}
+__device__ __forceinline__ void pin(const f32x16& a, const f32x16& b) {
+  asm volatile("" ::"v"(a), "v"(b));
+}
+__device__ __forceinline__ void pin(const f32x16 (&o)[4]) {
+  asm volatile("" ::"v"(o[0]), "v"(o[1]), "v"(o[2]), "v"(o[3]));
+}
+
+template <bool SET_M>
+__device__ __forceinline__ void pp_vphase(WaveAttn& st, f32x16& s0, f32x16& s1, int k,
+                                          int n_unm, int lim_abs, int h2, u32x4 (&pb)[4]) {
+  if (k >= n_unm) WaveAttn::mask(s0, s1, k * kKeyTile, lim_abs, h2);
+  if (SET_M && k == 0) st.m = WaveAttn::row_max(s0, s1);
+  st.probs<false>(s0, s1, k * kKeyTile, lim_abs, h2, pb);
+  pin(pb, st.lsum);
+}
+
+// M(k+1) with the buffers of parity PAR = k & 1: P.V of tile k from
+// v[PAR], then Q.K of tile k+1 from k[1-PAR].
+template <int PAR>
+__device__ __forceinline__ void pp_mphase(WaveAttn& st, const AttnLds& lds, uint32_t kbt,
+                                          uint32_t vbt, const u32x4 (&qb)[8],
+                                          const u32x4 (&pb)[4], f32x16& s0, f32x16& s1,
+                                          bool has_next) {
+  // after the last tile the QK product reads a stale buffer; its result is unused
+  (void)has_next;
+  st.pv_qk<true>(PAR ? lds.v1 : lds.v0, vbt, pb, PAR ? lds.k0 : lds.k1, kbt, qb, s0, s1);
+  pin(s0, s1);
+  pin(st.o);
+}
+
+template <bool IS_B, bool SET_M>
+__device__ __forceinline__ void pingpong(WaveAttn& st, const TileLoader<4>& ld,
+                                         const AttnLds& lds, const uint16_t* kbase,
+                                         const uint16_t* vbase, int64_t sp, int kend,
+                                         int n_kt, int n_unm, const u32x4 (&qb)[8],
+                                         int lim_abs, int h2) {
+  uint32_t kbt, vbt;
+  st.offsets(kbt, vbt);
+  f32x16 s0, s1;
+  u32x4 pb[4];
+  // phase 0 (K tile 0 is in k0 and visible).  Group B, whose even phases
+  // are its exponential phases, issues every tile copy; group A only computes.
+  if (IS_B) pp_loads<0>(ld, lds, kbase, vbase, sp, kend, 0, n_kt);
+  if (!IS_B) {
+    WaveAttn::qk(lds.k0, kbt, qb, s0, s1);
+    pin(s0, s1);
+  }
+  __syncthreads();
+  if (IS_B) {  // phase 1
+    WaveAttn::qk(lds.k0, kbt, qb, s0, s1);
+    pin(s0, s1);
+    wait_tile_loads();
+    __syncthreads();
+  }
+  for (int k = 0; k < n_kt; k += 2) {
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int kk = k + par;
+      if (par == 1 && kk >= n_kt) break;
+      if (!IS_B) {
+        pp_vphase<SET_M>(st, s0, s1, kk, n_unm, lim_abs, h2, pb);  // phase 2kk+1
+        wait_tile_loads();
+        __syncthreads();
+        if (par == 0)  // phase 2kk+2
+          pp_mphase<0>(st, lds, kbt, vbt, qb, pb, s0, s1, kk + 1 < n_kt);
+        else
+          pp_mphase<1>(st, lds, kbt, vbt, qb, pb, s0, s1, kk + 1 < n_kt);
+        __syncthreads();
+      } else {
+        if (par == 0) pp_loads<1>(ld, lds, kbase, vbase, sp, kend, kk + 1, n_kt);
+        else pp_loads<0>(ld, lds, kbase, vbase, sp, kend, kk + 1, n_kt);
+        pp_vphase<SET_M>(st, s0, s1, kk, n_unm, lim_abs, h2, pb);  // phase 2kk+2
+        __syncthreads();
+        if (par == 0) pp_mphase<0>(st, lds, kbt, vbt, qb, pb, s0, s1, kk + 1 < n_kt);
+        else pp_mphase<1>(st, lds, kbt, vbt, qb, pb, s0, s1, kk + 1 < n_kt);
+        wait_tile_loads();  // phase 2kk+3
+        __syncthreads();
+      }
+    }
+  }
+  if (!IS_B) {  // phase 2 n_kt + 1: group B's last M phase
+    wait_tile_loads();
+    __syncthreads();
+  }
+}
+
+template <bool SET_M>
+__device__ __forceinline__ void attend_pp(WaveAttn& st, const TileLoader<4>& ld,
+                                          const AttnLds& lds, const uint16_t* kbase,
+                                          const uint16_t* vbase, int64_t sp, int kend,
+                                          int n_kt, int n_unm, const u32x4 (&qb)[8],
+                                          int lim_abs, int h2, bool is_b) {
+  if (is_b) pingpong<true, SET_M>(st, ld, lds, kbase, vbase, sp, kend, n_kt, n_unm, qb, lim_abs, h2);
+  else pingpong<false, SET_M>(st, ld, lds, kbase, vbase, sp, kend, n_kt, n_unm, qb, lim_abs, h2);
+}
+
+// Blocks are ordered heaviest q-tile first; when the number of (sequence, kv
+// head) pairs is a multiple of 8, all tiles of a pair land on one XCD (the
+// hardware deals workgroup ids to the 8 XCDs round robin), so its K/V stay
+// in that XCD's L2.
+template <int G>
+__global__ __launch_bounds__(512, 1) void prefill_attn_kernel(PrefillArgs a) {
+  constexpr int TQ = 256 / G;            // tokens per workgroup
+  constexpr int NPOS = (TQ + 63) / 64;   // positions per lane (each wave reads all)
+  __shared__ __attribute__((aligned(16))) unsigned char lds_k0[kKTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_k1[kKTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_v0[kKTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_v1[kKTileBytes];
+  const AttnLds lds{lds_k0, lds_k1, lds_v0, lds_v1};
+
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = l & 31, h2 = l >> 5;
 
   const int n_pairs = a.n_seq * a.n_kv_heads;
@@ -103,20 +303,25 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillArgs a) {
   const bool tok_ok = tl < n_tok;
   const int t = tok0 + tl;
 
-  // Positions of the block's tokens: every wave reads all of them (TQ <= 128)
-  // and reduces in registers, so no LDS round trip or barrier is needed.
-  // The q-side reads go out together with them.
-  int pv0 = -1, pv1 = -1;
-  if (l < n_tok) pv0 = a.positions[tok0 + l];
-  if (TQ > 64 && l + 64 < n_tok) pv1 = a.positions[tok0 + l + 64];
+  // Positions of the block's tokens: every wave reads all of them and
+  // reduces in registers (no LDS round trip or barrier).  The q-side reads
+  // go out together with them.
+  int pv[NPOS];
+#pragma unroll
+  for (int i = 0; i < NPOS; ++i)
+    pv[i] = (l + 64 * i < n_tok) ? a.positions[tok0 + l + 64 * i] : -1;
   QPrologue qp;
   qp.load(a.q + (size_t)t * a.q_tok_stride + (size_t)h * kHeadDim, tok_ok,
           a.cs + (size_t)(tok_ok ? t : 0) * kHalf, a.q_norm_w, h2);
 
   const int cap = a.c.capacity;
-  const bool v0 = pv0 >= 0 && pv0 < cap, v1 = pv1 >= 0 && pv1 < cap;
-  int kv_end = max(v0 ? pv0 + 1 : 0, v1 ? pv1 + 1 : 0);
-  int pmin = min(v0 ? pv0 : INT_MAX, v1 ? pv1 : INT_MAX);
+  int kv_end = 0, pmin = INT_MAX;
+#pragma unroll
+  for (int i = 0; i < NPOS; ++i) {
+    const bool v = pv[i] >= 0 && pv[i] < cap;
+    kv_end = max(kv_end, v ? pv[i] + 1 : 0);
+    pmin = min(pmin, v ? pv[i] : INT_MAX);
+  }
 #pragma unroll
   for (int sh = 1; sh < 64; sh <<= 1) {
     kv_end = max(kv_end, __shfl_xor(kv_end, sh));
@@ -125,8 +330,13 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillArgs a) {
   // wave-uniform (the tile loader's buffer descriptors must live in SGPRs)
   kv_end = __builtin_amdgcn_readfirstlane(kv_end);
   pmin = __builtin_amdgcn_readfirstlane(pmin);
-  const int pa = __shfl(pv0, tl & 63), pb = __shfl(pv1, tl & 63);
-  int p = !tok_ok ? -1 : (tl < 64 ? pa : pb);
+  int p = -1;
+#pragma unroll
+  for (int i = 0; i < NPOS; ++i) {
+    const int pi = __shfl(pv[i], tl & 63);
+    if (tl / 64 == i) p = pi;
+  }
+  if (!tok_ok) p = -1;
   const bool q_ok = tok_ok && p >= 0 && p < cap;
   if (!q_ok) p = kv_end - 1;  // sees every key; its output is not kept
 
@@ -146,20 +356,34 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillArgs a) {
 
   const uint16_t* kbase = a.c.k + (size_t)seq * a.c.sb + (size_t)g * a.c.sh;
   const uint16_t* vbase = a.c.v + (size_t)seq * a.c.sb + (size_t)g * a.c.sh;
+  const int n_kt = (kv_end + kKeyTile - 1) / kKeyTile;
+  // tiles wholly at or below the smallest position need no mask
+  const int n_unm = min((pmin + 1) / kKeyTile, n_kt);
 
-  TileLoader<4> ld;
-  ld.init(__builtin_amdgcn_readfirstlane(w), l, a.c.sp);
-  load_first(ld, stage0, kbase, vbase, a.c.sp, 0, kv_end);
+  TileLoader<8> ld;  // all waves: first tile, exact-max pass
+  ld.init(w, l, a.c.sp);
+  TileLoader<4> ldb;  // group B: the tile copies of the ping-pong
+  ldb.init(w & 3, l, a.c.sp);
+  ld.load_k(kbase, a.c.sp, 0, kv_end, lds.k0);
 
   u32x4 qb[8];
   qp.compute((float)a.eps, a.qscale, qb);
 
   WaveAttn st;
   st.init(l);
-  // tiles wholly at or below the smallest position need no mask
-  const int n_unmasked = (pmin + 1) / kKeyTile;
-  attend_tiles(st, ld, stage0, stage1, kbase, vbase, a.c.sp, 0, kv_end, n_unmasked, qb,
-               p, h2);
+  wait_tile_loads();
+  __syncthreads();
+  const bool is_b = w >= 4;
+  attend_pp<true>(st, ldb, lds, kbase, vbase, a.c.sp, kv_end, n_kt, n_unm, qb, p, h2, is_b);
+  if (__syncthreads_or(st.overflowed())) {
+    // a later score far above the first tile's max: redo with the exact one
+    st.m = exact_row_max(st, ld, lds, kbase, a.c.sp, 0, kv_end, qb, p, h2);
+    st.reset();
+    ld.load_k(kbase, a.c.sp, 0, kv_end, lds.k0);
+    wait_tile_loads();
+    __syncthreads();
+    attend_pp<false>(st, ldb, lds, kbase, vbase, a.c.sp, kv_end, n_kt, n_unm, qb, p, h2, is_b);
+  }
 
   const float lt = st.lsum + __shfl_xor(st.lsum, 32);
   const float inv = q_ok ? 1.0f / lt : 0.f;
@@ -191,14 +415,14 @@ hipError_t launch_prefill(const PrefillArgs& a0, const RopeFreq& f, int group,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   ++*n_kernels;
-  const int tq = 128 / group;
+  const int tq = 256 / group;
   a.n_qtiles = (a.max_seqlen + tq - 1) / tq;
   const dim3 grid((unsigned)(a.n_seq * a.n_kv_heads * a.n_qtiles));
   switch (group) {
-    case 1: hipLaunchKernelGGL(prefill_attn_kernel<1>, grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(prefill_attn_kernel<2>, grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(prefill_attn_kernel<4>, grid, dim3(256), 0, s, a); break;
-    case 8: hipLaunchKernelGGL(prefill_attn_kernel<8>, grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL(prefill_attn_kernel<1>, grid, dim3(512), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(prefill_attn_kernel<2>, grid, dim3(512), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(prefill_attn_kernel<4>, grid, dim3(512), 0, s, a); break;
+    case 8: hipLaunchKernelGGL(prefill_attn_kernel<8>, grid, dim3(512), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   e = hipGetLastError();

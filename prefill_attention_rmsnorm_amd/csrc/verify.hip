@@ -20,8 +20,11 @@ namespace qa {
 template <int G, int NW>
 __global__ __launch_bounds__(NW * 64) void verify_kernel(DecodeArgs a, RopeFreq f) {
   constexpr int NT = NW * 64;
-  __shared__ __attribute__((aligned(16))) unsigned char stage0[kStageBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char stage1[kStageBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_k0[kKTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_k1[kKTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_v0[kKTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_v1[kKTileBytes];
+  const AttnLds lds{lds_k0, lds_k1, lds_v0, lds_v1};
   __shared__ __attribute__((aligned(16))) float2 cs[(128 / G) * kHalf];  // [draft token][pair]
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
@@ -92,13 +95,12 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(DecodeArgs a, RopeFreq 
     ld.init(__builtin_amdgcn_readfirstlane(w), l, a.c.sp);
     WaveAttn st;
     st.init(l);
-    load_first(ld, stage0, kbase, vbase, a.c.sp, k0, k1);
+    load_first(ld, lds, kbase, vbase, a.c.sp, k0, k1);
     const int lim_abs = row_ok ? min(p, k1 - 1) : k1 - 1;
     // tiles whose keys all lie below k1 and at or below the first draft
     // position need no mask
     const int n_unmasked = max(min(k1 - 1, L0) + 1 - k0, 0) / kKeyTile;
-    attend_tiles(st, ld, stage0, stage1, kbase, vbase, a.c.sp, k0, k1, n_unmasked, qb,
-                 lim_abs, h2);
+    attend(st, ld, lds, kbase, vbase, a.c.sp, k0, k1, n_unmasked, qb, lim_abs, h2);
     if (row_ok) {
       const float lt = st.lsum + __shfl_xor(st.lsum, 32);
       if (h2 == 0) {
