@@ -181,9 +181,7 @@ size_t qa_workspace_bytes(int op, int batch, int n_q_heads, int n_kv_heads,
       return qa::prefill_ws_bytes(max_ctx);
     case QA_OP_DECODE:
       if (max_ctx < 1) return 0;
-      return qa::split_layout(batch, n_kv_heads, G, max_ctx,
-                              qa::decode_keys_per_split(batch, n_kv_heads, max_ctx))
-          .total;
+      return qa::decode_split_layout(batch, n_kv_heads, G, max_ctx).total;
     case QA_OP_VERIFY:
       if (max_ctx < 1 || block_len < 1 || block_len * G > 128) return 0;
       return qa::split_layout(batch, n_kv_heads, block_len * G, max_ctx,
@@ -327,9 +325,7 @@ qa_status qa_decode(const qa_cache* c, const qa_params* p, const void* q,
   QA_REQUIRE(al16(q) && al16(k) && al16(v) && al16(out) && al16(ws) && al4(lse) &&
                  al4(positions),
              QA_ERR_ALIGN, "q/k/v/out/ws must be 16-byte aligned");
-  const qa::SplitLayout L = qa::split_layout(
-      batch, c->n_kv_heads, G, max_ctx,
-      qa::decode_keys_per_split(batch, c->n_kv_heads, max_ctx));
+  const qa::SplitLayout L = qa::decode_split_layout(batch, c->n_kv_heads, G, max_ctx);
   QA_REQUIRE(ws_bytes >= L.total, QA_ERR_WORKSPACE,
              "workspace %zu bytes < %zu needed", ws_bytes, L.total);
   qa::DecodeArgs a;

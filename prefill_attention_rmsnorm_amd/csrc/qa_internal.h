@@ -32,15 +32,25 @@ struct SplitLayout {
   size_t m_off, l_off, o_off, total;
 };
 
-// Decode: keys per split-K block.  Small grids use short splits so more
-// workgroups stream the cache; the count is a function of the launch sizes
-// only (never of device-side positions), so graphs stay valid.
+// Decode: keys per split-K block, a multiple of 16 (one score tile) of at
+// most kDecodeMaxTiles tiles.  The split count aims at kDecodeBlocks
+// workgroups in all (two 256-thread workgroups per CU of a 256-CU part) and
+// does not pass it unless the split would exceed kDecodeMaxTiles, so every CU
+// streams the same number of cache bytes: a grid a few blocks over a multiple
+// of the CU count leaves those CUs a third block to stream after the rest
+// have finished.  The split is a function of the launch
+// sizes only (never of device-side positions), so graphs stay valid.
+constexpr int kDecodeBlocks = 512;
+constexpr int kDecodeMaxTiles = 16;
 inline int decode_keys_per_split(int batch, int n_kv, int max_ctx) {
   long pairs = (long)batch * n_kv;
-  int ks = 64;
-  // grow the split while the grid would still exceed ~2 workgroups per CU
-  while (ks < 128 && pairs * ((max_ctx + 2 * ks - 1) / (2 * ks)) >= 512) ks *= 2;
-  return ks;
+  long want = kDecodeBlocks / pairs;  // splits per (sequence, kv head)
+  if (want < 1) want = 1;
+  long ks = (max_ctx + want - 1) / want;
+  ks = (ks + 15) / 16 * 16;
+  if (ks < 16) ks = 16;
+  if (ks > 16 * kDecodeMaxTiles) ks = 16 * kDecodeMaxTiles;
+  return (int)ks;
 }
 
 // Verify: about one workgroup per CU in total; splits are whole 64-key tiles.
@@ -52,12 +62,14 @@ inline int verify_keys_per_split(int batch, int n_kv, int max_ctx) {
   return ks < kKeyTile ? kKeyTile : (int)ks;
 }
 
+// extra: partials beyond the cache splits (decode adds one for the new token).
 inline SplitLayout split_layout(int batch, int n_kv, int rows, int max_ctx,
-                                int keys_per_split) {
+                                int keys_per_split, int extra = 0) {
   SplitLayout L;
   L.keys_per_split = keys_per_split;
   L.n_split = (max_ctx + keys_per_split - 1) / keys_per_split;
   if (L.n_split < 1) L.n_split = 1;
+  L.n_split += extra;
   size_t pairs = (size_t)batch * n_kv;
   size_t nrow = pairs * L.n_split * rows;
   L.m_off = kWsHeader;
@@ -65,6 +77,14 @@ inline SplitLayout split_layout(int batch, int n_kv, int rows, int max_ctx,
   L.o_off = L.l_off + round256(nrow * sizeof(float));
   L.total = L.o_off + round256(nrow * kHeadDim * sizeof(float));
   return L;
+}
+
+// Decode partials: the cache splits (rows before the new slot) and one for
+// the new token.
+inline SplitLayout decode_split_layout(int batch, int n_kv, int G, int max_ctx) {
+  const int rows_before = max_ctx > 1 ? max_ctx - 1 : 1;
+  return split_layout(batch, n_kv, G, rows_before,
+                      decode_keys_per_split(batch, n_kv, rows_before), 1);
 }
 
 inline size_t prefill_ws_bytes(int total_tokens) {

@@ -95,6 +95,15 @@ def test_norm_weights():
     run_steps(2, 8, 2, 300, [100, 257], 2, seed=25, weights=True)
 
 
+@pytest.mark.parametrize("tiles", range(1, 17))
+def test_every_split_length(tiles):
+    # 2 sequences x 8 kv heads: 32 cache splits per pair, so max_ctx = 512 t
+    # gives runs of up to 16 t rows -- each split length the kernel is built
+    # for.  One sequence fills the context, the other a third of it.
+    B, Hq, Hkv, cap = 2, 32, 8, 512 * tiles
+    run_steps(B, Hq, Hkv, cap, [cap - 1, cap // 3], 1, 40 + tiles)
+
+
 def test_split_count_invariance():
     # The same step with max_ctx = context (few splits) and max_ctx = capacity
     # (more, partly empty splits) agrees to fp32 reordering noise.
