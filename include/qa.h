@@ -156,6 +156,9 @@ qa_status qa_workspace_init(void* ws, size_t ws_bytes, void* stream);
  *   out bf16 [total_tokens][n_q_heads][128] (dense)
  *   lse fp32 [total_tokens][n_q_heads] natural-log log-sum-exp, or NULL
  *   max_seqlen >= every sequence length (sizes the launch grid)
+ *   ws  workspace of qa_workspace_bytes(QA_OP_PREFILL, ..., total_tokens, 0)
+ *       bytes: the error word and the queries' cos/sin table (8 bytes per
+ *       token and rotation pair), written and read within the call
  * total_tokens == 0 is a valid no-op.
  */
 qa_status qa_prefill(const qa_cache* c, const qa_params* p, const void* q,

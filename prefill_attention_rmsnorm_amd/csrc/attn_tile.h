@@ -515,6 +515,36 @@ struct QPrologue {
     }
   }
 
+  // q and norm weights only; the cos/sin then come from cs_from_lds().
+  __device__ __forceinline__ void load_qw(const uint16_t* qrow, bool valid,
+                                          const uint16_t* wq, int h2) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      q[ks] = u32x4{0u, 0u, 0u, 0u};
+      if (valid) q[ks] = ld16(qrow + 16 * ks + 8 * h2);
+    }
+    const uint32_t one2 = 0x3F803F80u;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      w[ks] = u32x4{one2, one2, one2, one2};
+      if (wq) w[ks] = ld16(wq + 64 * (ks >> 2) + 16 * (ks & 3) + 8 * h2);
+    }
+  }
+
+  // cos/sin of the lane's pairs from an LDS copy of the block's table rows:
+  // row tl (512 bytes, 32 chunks of two pairs) holds chunk c at chunk
+  // position c ^ (tl & 31).
+  __device__ __forceinline__ void cs_from_lds(const unsigned char* rows, int tl, int h2) {
+    const unsigned char* row = rows + tl * 512;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = 8 * ks + 4 * h2 + u;
+        cs[4 * ks + u] = *reinterpret_cast<const float4*>(row + 16 * (c ^ (tl & 31)));
+      }
+  }
+
   __device__ __forceinline__ void compute(float eps, float qscale,
                                           u32x4 (&qb)[8]) const {
     float x[8][8];

@@ -20,30 +20,105 @@ namespace qa {
 // two 16-byte pieces.  The head's sum of squares is then a 3-step reduction
 // inside the group (exact in fp64 for bf16 inputs of moderate range, so its
 // order does not matter), and the arithmetic per element is the fp64
-// sequence x / r * w, rotation, one round to bf16.
+// sequence x / r * w, rotation, one round to bf16.  A token whose position is
+// out of range writes no cache slot.
+// k' and v of one KV head into its cache slot: lane sub holds dims
+// 8*sub .. +7 (ka, va) and 64 + 8*sub .. +7 (kb, vb); the eight lanes of the
+// head reduce the sum of squares in fp64.
+__device__ __forceinline__ void kv_head(uint16_t* ck, uint16_t* cv, int sub, u32x4 ka,
+                                        u32x4 kb, u32x4 va, u32x4 vb, const double (&w0)[8],
+                                        const double (&w1)[8], const double (&cs_c)[8],
+                                        const double (&cs_s)[8], double eps, bool active) {
+  double x0[8], x1[8];
+#pragma unroll
+  for (int e2 = 0; e2 < 4; ++e2) {
+    x0[2 * e2] = bf_lo(ka[e2]); x0[2 * e2 + 1] = bf_hi(ka[e2]);
+    x1[2 * e2] = bf_lo(kb[e2]); x1[2 * e2 + 1] = bf_hi(kb[e2]);
+  }
+  u32x4 oa, ob;
+  {
+#pragma clang fp contract(off)
+    double ss = 0.0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += x0[e] * x0[e] + x1[e] * x1[e];
+    ss += __shfl_xor(ss, 1);
+    ss += __shfl_xor(ss, 2);
+    ss += __shfl_xor(ss, 4);
+    const double r = sqrt(ss / 128.0 + eps);
+    uint16_t o0[8], o1[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const double y0 = x0[e] / r * w0[e];
+      const double y1 = x1[e] / r * w1[e];
+      o0[e] = f64_to_bf16_rne(y0 * cs_c[e] - y1 * cs_s[e]);
+      o1[e] = f64_to_bf16_rne(y1 * cs_c[e] + y0 * cs_s[e]);
+    }
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      oa[e2] = (uint32_t)o0[2 * e2] | ((uint32_t)o0[2 * e2 + 1] << 16);
+      ob[e2] = (uint32_t)o1[2 * e2] | ((uint32_t)o1[2 * e2 + 1] << 16);
+    }
+  }
+  if (active) {
+    st16(ck + 8 * sub, oa);
+    st16(ck + 64 + 8 * sub, ob);
+    st16(cv + 8 * sub, va);
+    st16(cv + 64 + 8 * sub, vb);
+  }
+}
+
+__device__ __forceinline__ void bf16x8_to_f64(u32x4 w, double (&d)[8]) {
+#pragma unroll
+  for (int e2 = 0; e2 < 4; ++e2) {
+    d[2 * e2] = bf_lo(w[e2]);
+    d[2 * e2 + 1] = bf_hi(w[e2]);
+  }
+}
+
 __global__ __launch_bounds__(256) void kv_prologue_kernel(PrefillArgs a,
                                                           RopeFreq f) {
   __shared__ double2 s_cs[4][kHalf];  // per wave: (cos, sin) of the 64 pairs
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wv;
   if (t >= a.total_tokens) return;
-  const int pos = a.positions[t];
+  const int gh = lane >> 3, sub = lane & 7;
 
+  // ---- every load first: the work of a token is a few short dependent
+  // steps, so the memory latency is paid once per wave, not once per step.
+  const int pos = a.positions[t];
+  const double invf = f.inv_freq[lane];  // (a lane-indexed kernel-argument load)
+  const int cuv = lane <= a.n_seq ? a.cu_seqlens[lane] : INT_MAX;
+  const u32x4 one8 = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  const uint16_t* kwp = a.k_norm_w ? a.k_norm_w : a.q;
+  const u32x4 kwa = ld16(kwp + 8 * sub), kwb = ld16(kwp + 64 + 8 * sub);
+  const bool kact = gh < a.n_kv_heads;
+  const size_t ksrc = (size_t)t * a.kv_tok_stride + (size_t)(kact ? gh : 0) * kHeadDim;
+  const u32x4 ka = ld16(a.k + ksrc + 8 * sub), kb = ld16(a.k + ksrc + 64 + 8 * sub);
+  const u32x4 va = ld16(a.v + ksrc + 8 * sub), vb = ld16(a.v + ksrc + 64 + 8 * sub);
+
+  // ---- cos/sin of the token's 64 angles (fp64), one pair per lane
   {
     double sn = 0.0, cn = 1.0;
-    const double ang = (double)pos * f.inv_freq[lane];
-    sincos(ang, &sn, &cn);
+    sincos((double)pos * invf, &sn, &cn);
     a.cs[(size_t)t * kHalf + lane] = make_float2((float)cn, (float)sn);
     s_cs[wv][lane] = make_double2(cn, sn);
   }
 
-  // sequence owning token t: the last i with cu[i] <= t
-  int lo = 0, hi = a.n_seq;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.cu_seqlens[mid] <= t) lo = mid; else hi = mid;
+  // ---- sequence owning token t: the number of boundaries cu[1..n_seq] at
+  // or below t (one ballot for up to 63 sequences, else a binary search)
+  int seq;
+  if (a.n_seq < 64) {
+    seq = __popcll(__ballot(lane >= 1 && lane <= a.n_seq && cuv <= t));
+  } else {
+    int lo = 0, hi = a.n_seq;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.cu_seqlens[mid] <= t) lo = mid; else hi = mid;
+    }
+    seq = lo;
   }
-  const int c0 = a.cu_seqlens[lo], c1 = a.cu_seqlens[lo + 1];
+  seq = min(seq, a.n_seq - 1);
+  const int c0 = a.cu_seqlens[seq], c1 = a.cu_seqlens[seq + 1];
   if (!(c0 <= t && t < c1 && c1 - c0 <= a.max_seqlen)) {
     if (lane == 0) flag_error(a.err, QA_DEVERR_SEQLENS);
     return;
@@ -52,20 +127,7 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(PrefillArgs a,
     if (lane == 0) flag_error(a.err, QA_DEVERR_POSITION);
     return;
   }
-  const int gh = lane >> 3, sub = lane & 7;
-  double w0[8], w1[8];
-  {
-    u32x4 wa = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u}, wb = wa;
-    if (a.k_norm_w) {
-      wa = ld16(a.k_norm_w + 8 * sub);
-      wb = ld16(a.k_norm_w + 64 + 8 * sub);
-    }
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-      w0[2 * e2] = bf_lo(wa[e2]); w0[2 * e2 + 1] = bf_hi(wa[e2]);
-      w1[2 * e2] = bf_lo(wb[e2]); w1[2 * e2 + 1] = bf_hi(wb[e2]);
-    }
-  }
+
   __builtin_amdgcn_wave_barrier();  // s_cs of this wave written
   double cs_c[8], cs_s[8];
 #pragma unroll
@@ -74,51 +136,22 @@ __global__ __launch_bounds__(256) void kv_prologue_kernel(PrefillArgs a,
     cs_c[e] = v.x;
     cs_s[e] = v.y;
   }
-  const size_t row0 = (size_t)lo * a.c.sb + (size_t)pos * a.c.sp;
-  for (int g0 = 0; g0 < a.n_kv_heads; g0 += 8) {
+
+  // ---- k' and v of every KV head (eight at a time)
+  double kw0[8], kw1[8];
+  bf16x8_to_f64(a.k_norm_w ? kwa : one8, kw0);
+  bf16x8_to_f64(a.k_norm_w ? kwb : one8, kw1);
+  const size_t row0 = (size_t)seq * a.c.sb + (size_t)pos * a.c.sp;
+  kv_head(a.c.k + row0 + (size_t)gh * a.c.sh, a.c.v + row0 + (size_t)gh * a.c.sh, sub, ka,
+          kb, va, vb, kw0, kw1, cs_c, cs_s, a.eps, kact);
+  for (int g0 = 8; g0 < a.n_kv_heads; g0 += 8) {
     const int g = g0 + gh;
-    const bool active = g < a.n_kv_heads;  // a whole lane group at once
-    const size_t src = (size_t)t * a.kv_tok_stride + (size_t)(active ? g : 0) * kHeadDim;
-    const u32x4 ka = ld16(a.k + src + 8 * sub), kb = ld16(a.k + src + 64 + 8 * sub);
-    const u32x4 va = ld16(a.v + src + 8 * sub), vb = ld16(a.v + src + 64 + 8 * sub);
-    double x0[8], x1[8];
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-      x0[2 * e2] = bf_lo(ka[e2]); x0[2 * e2 + 1] = bf_hi(ka[e2]);
-      x1[2 * e2] = bf_lo(kb[e2]); x1[2 * e2 + 1] = bf_hi(kb[e2]);
-    }
-    u32x4 oa, ob;
-    {
-#pragma clang fp contract(off)
-      double ss = 0.0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss += x0[e] * x0[e] + x1[e] * x1[e];
-      ss += __shfl_xor(ss, 1);
-      ss += __shfl_xor(ss, 2);
-      ss += __shfl_xor(ss, 4);
-      const double r = sqrt(ss / 128.0 + a.eps);
-      uint16_t o0[8], o1[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const double y0 = x0[e] / r * w0[e];
-        const double y1 = x1[e] / r * w1[e];
-        o0[e] = f64_to_bf16_rne(y0 * cs_c[e] - y1 * cs_s[e]);
-        o1[e] = f64_to_bf16_rne(y1 * cs_c[e] + y0 * cs_s[e]);
-      }
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        oa[e2] = (uint32_t)o0[2 * e2] | ((uint32_t)o0[2 * e2 + 1] << 16);
-        ob[e2] = (uint32_t)o1[2 * e2] | ((uint32_t)o1[2 * e2 + 1] << 16);
-      }
-    }
-    if (active) {
-      uint16_t* ck = a.c.k + row0 + (size_t)g * a.c.sh;
-      uint16_t* cv = a.c.v + row0 + (size_t)g * a.c.sh;
-      st16(ck + 8 * sub, oa);
-      st16(ck + 64 + 8 * sub, ob);
-      st16(cv + 8 * sub, va);
-      st16(cv + 64 + 8 * sub, vb);
-    }
+    const bool act = g < a.n_kv_heads;
+    const size_t src = (size_t)t * a.kv_tok_stride + (size_t)(act ? g : 0) * kHeadDim;
+    kv_head(a.c.k + row0 + (size_t)g * a.c.sh, a.c.v + row0 + (size_t)g * a.c.sh, sub,
+            ld16(a.k + src + 8 * sub), ld16(a.k + src + 64 + 8 * sub),
+            ld16(a.v + src + 8 * sub), ld16(a.v + src + 64 + 8 * sub), kw0, kw1, cs_c,
+            cs_s, a.eps, act);
   }
 }
 
@@ -166,6 +199,18 @@ __device__ __forceinline__ void pin(const f32x16 (&o)[4]) {
   asm volatile("" ::"v"(o[0]), "v"(o[1]), "v"(o[2]), "v"(o[3]));
 }
 
+// The barrier between ping-pong phases.  __syncthreads() fences workgroup
+// memory, and the fence waits for every copy into LDS still in flight, which
+// would expose the copy latency in the phase that issues them instead of
+// hiding it behind the next one.  Here the copies that a phase hands on are
+// waited for explicitly (wait_tile_loads) by the waves that issued them, so
+// the barrier itself only has to order LDS reads: this wave's are drained
+// (lgkmcnt) and the "memory" clobber keeps the compiler from moving LDS
+// accesses across it.
+__device__ __forceinline__ void phase_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <bool SET_M>
 __device__ __forceinline__ void pp_vphase(WaveAttn& st, f32x16& s0, f32x16& s1, int k,
                                           int n_unm, int lim_abs, int h2, u32x4 (&pb)[4]) {
@@ -199,19 +244,20 @@ __device__ __forceinline__ void pingpong(WaveAttn& st, const TileLoader<4>& ld,
   st.offsets(kbt, vbt);
   f32x16 s0, s1;
   u32x4 pb[4];
-  // phase 0 (K tile 0 is in k0 and visible).  Group B, whose even phases
-  // are its exponential phases, issues every tile copy; group A only computes.
-  if (IS_B) pp_loads<0>(ld, lds, kbase, vbase, sp, kend, 0, n_kt);
+  // phase 0 (K tile 0 is in k0 and visible; K tile 1 and V tile 0 were
+  // issued with it by every wave, see load_next_two).  From here on group B,
+  // whose even phases are its exponential phases, issues every tile copy;
+  // group A only computes.
   if (!IS_B) {
     WaveAttn::qk(lds.k0, kbt, qb, s0, s1);
     pin(s0, s1);
   }
-  __syncthreads();
+  phase_barrier();
   if (IS_B) {  // phase 1
     WaveAttn::qk(lds.k0, kbt, qb, s0, s1);
     pin(s0, s1);
     wait_tile_loads();
-    __syncthreads();
+    phase_barrier();
   }
   for (int k = 0; k < n_kt; k += 2) {
 #pragma unroll
@@ -221,28 +267,66 @@ __device__ __forceinline__ void pingpong(WaveAttn& st, const TileLoader<4>& ld,
       if (!IS_B) {
         pp_vphase<SET_M>(st, s0, s1, kk, n_unm, lim_abs, h2, pb);  // phase 2kk+1
         wait_tile_loads();
-        __syncthreads();
+        phase_barrier();
         if (par == 0)  // phase 2kk+2
           pp_mphase<0>(st, lds, kbt, vbt, qb, pb, s0, s1, kk + 1 < n_kt);
         else
           pp_mphase<1>(st, lds, kbt, vbt, qb, pb, s0, s1, kk + 1 < n_kt);
-        __syncthreads();
+        phase_barrier();
       } else {
         if (par == 0) pp_loads<1>(ld, lds, kbase, vbase, sp, kend, kk + 1, n_kt);
         else pp_loads<0>(ld, lds, kbase, vbase, sp, kend, kk + 1, n_kt);
         pp_vphase<SET_M>(st, s0, s1, kk, n_unm, lim_abs, h2, pb);  // phase 2kk+2
-        __syncthreads();
+        phase_barrier();
         if (par == 0) pp_mphase<0>(st, lds, kbt, vbt, qb, pb, s0, s1, kk + 1 < n_kt);
         else pp_mphase<1>(st, lds, kbt, vbt, qb, pb, s0, s1, kk + 1 < n_kt);
         wait_tile_loads();  // phase 2kk+3
-        __syncthreads();
+        phase_barrier();
       }
     }
   }
   if (!IS_B) {  // phase 2 n_kt + 1: group B's last M phase
     wait_tile_loads();
-    __syncthreads();
+    phase_barrier();
   }
+}
+
+// The cos/sin rows (512 bytes each) of the block's TQ tokens into LDS, for
+// blocks of four or more heads per token (their rows are then shared by that
+// many lanes, which would otherwise each read them from L2).  Chunk c of row
+// r lands at chunk position c ^ (r & 31), so a wave reading one chunk of 32
+// rows hits distinct banks: a copy places lane L at 16 L, so lane L fetches
+// the chunk that belongs there.  Rows at or past n_tok read as zero.
+template <int TQ>
+__device__ __forceinline__ void load_cs_rows(const float2* cs, int tok0, int n_tok,
+                                             unsigned char* dst, int w, int l) {
+  constexpr int NPIECE = TQ / 2;  // 1 KiB copies, two rows each
+  static_assert(NPIECE % 8 == 0, "rows per block");
+  const int nrec = __builtin_amdgcn_readfirstlane(n_tok * 512);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(cs + (size_t)tok0 * kHalf), 0, nrec, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < NPIECE / 8; ++i) {
+    const int piece = w + 8 * i;
+    const int r = 2 * piece + (l >> 5);
+    const int c = (l & 31) ^ (r & 31);
+    buffer_load_lds16(rs, dst + piece * 1024, (uint32_t)(r * 512 + c * 16));
+  }
+}
+
+// K tile 1 and V tile 0 (the copies of the ping-pong's phase 0), issued by all
+// eight waves before the block's first barrier: two copies per tile and wave,
+// so four copies follow K tile 0 in every wave's memory counter.  K tile 1 is
+// copied even past kend (as zeros) to keep that count fixed.
+__device__ __forceinline__ void load_next_two(const TileLoader<8>& ld, const AttnLds& lds,
+                                              const uint16_t* kbase, const uint16_t* vbase,
+                                              int64_t sp, int kend) {
+  ld.load_k(kbase, sp, kKeyTile, kend, lds.k1);
+  ld.load_v(vbase, sp, 0, kend, lds.v0);
+}
+// Wait for every copy of this wave but the four of load_next_two.
+__device__ __forceinline__ void wait_first_tile() {
+  __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
 }
 
 template <bool SET_M>
@@ -267,6 +351,8 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char lds_k1[kKTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned char lds_v0[kKTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned char lds_v1[kKTileBytes];
+  constexpr bool CS_LDS = G >= 4;
+  __shared__ __attribute__((aligned(16))) unsigned char lds_cs[CS_LDS ? TQ * 512 : 16];
   const AttnLds lds{lds_k0, lds_k1, lds_v0, lds_v1};
 
   const int tid = threadIdx.x, l = tid & 63;
@@ -286,15 +372,29 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_kernel(PrefillArgs a) {
   }
   const int seq = pair / a.n_kv_heads, g = pair % a.n_kv_heads;
   const int qt = a.n_qtiles - 1 - qt_rev;
+  const uint16_t* kbase = a.c.k + (size_t)seq * a.c.sb + (size_t)g * a.c.sh;
+  const uint16_t* vbase = a.c.v + (size_t)seq * a.c.sb + (size_t)g * a.c.sh;
+
+  // K tile 0 first, ahead of the positions it would otherwise wait for: its
+  // rows are bounded by the capacity only, since a key at or past the block's
+  // last position is masked for every query by selection (so whatever such
+  // a row holds never reaches a result).  Every return below first drains it.
+  TileLoader<8> ld;  // all waves: the first copies, exact-max pass
+  ld.init(w, l, a.c.sp);
+  ld.load_k(kbase, a.c.sp, 0, a.c.capacity, lds.k0);
 
   const int s0 = a.cu_seqlens[seq], s1 = a.cu_seqlens[seq + 1];
   if (s0 < 0 || s1 < s0 || s1 > a.total_tokens || s1 - s0 > a.max_seqlen) {
     if (tid == 0) flag_error(a.err, QA_DEVERR_SEQLENS);
+    wait_tile_loads();
     return;
   }
   const int tok0 = s0 + qt * TQ;
   const int n_tok = min(TQ, s1 - tok0);
-  if (n_tok <= 0) return;
+  if (n_tok <= 0) {
+    wait_tile_loads();
+    return;
+  }
 
   // this lane's query column
   const int r = 32 * w + j;
@@ -311,8 +411,14 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_kernel(PrefillArgs a) {
   for (int i = 0; i < NPOS; ++i)
     pv[i] = (l + 64 * i < n_tok) ? a.positions[tok0 + l + 64 * i] : -1;
   QPrologue qp;
-  qp.load(a.q + (size_t)t * a.q_tok_stride + (size_t)h * kHeadDim, tok_ok,
-          a.cs + (size_t)(tok_ok ? t : 0) * kHalf, a.q_norm_w, h2);
+  if constexpr (CS_LDS) {
+    qp.load_qw(a.q + (size_t)t * a.q_tok_stride + (size_t)h * kHeadDim, tok_ok, a.q_norm_w,
+               h2);
+    load_cs_rows<TQ>(a.cs, tok0, n_tok, lds_cs, w, l);
+  } else {
+    qp.load(a.q + (size_t)t * a.q_tok_stride + (size_t)h * kHeadDim, tok_ok,
+            a.cs + (size_t)(tok_ok ? t : 0) * kHalf, a.q_norm_w, h2);
+  }
 
   const int cap = a.c.capacity;
   int kv_end = 0, pmin = INT_MAX;
@@ -342,6 +448,7 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_kernel(PrefillArgs a) {
 
   uint16_t* orow = a.out + ((size_t)t * a.n_q_heads + h) * kHeadDim;
   if (kv_end == 0) {  // no valid position in the tile
+    wait_tile_loads();
     if (tok_ok) {
       const u32x2 z = {0u, 0u};
 #pragma unroll
@@ -354,25 +461,25 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_kernel(PrefillArgs a) {
     return;
   }
 
-  const uint16_t* kbase = a.c.k + (size_t)seq * a.c.sb + (size_t)g * a.c.sh;
-  const uint16_t* vbase = a.c.v + (size_t)seq * a.c.sb + (size_t)g * a.c.sh;
   const int n_kt = (kv_end + kKeyTile - 1) / kKeyTile;
   // tiles wholly at or below the smallest position need no mask
   const int n_unm = min((pmin + 1) / kKeyTile, n_kt);
 
-  TileLoader<8> ld;  // all waves: first tile, exact-max pass
-  ld.init(w, l, a.c.sp);
   TileLoader<4> ldb;  // group B: the tile copies of the ping-pong
   ldb.init(w & 3, l, a.c.sp);
-  ld.load_k(kbase, a.c.sp, 0, kv_end, lds.k0);
+  load_next_two(ld, lds, kbase, vbase, a.c.sp, kv_end);
 
   u32x4 qb[8];
-  qp.compute((float)a.eps, a.qscale, qb);
+  if constexpr (!CS_LDS) qp.compute((float)a.eps, a.qscale, qb);
 
   WaveAttn st;
   st.init(l);
-  wait_tile_loads();
-  __syncthreads();
+  wait_first_tile();
+  phase_barrier();
+  if constexpr (CS_LDS) {  // the cos/sin rows are in LDS now
+    qp.cs_from_lds(lds_cs, tl, h2);
+    qp.compute((float)a.eps, a.qscale, qb);
+  }
   const bool is_b = w >= 4;
   attend_pp<true>(st, ldb, lds, kbase, vbase, a.c.sp, kv_end, n_kt, n_unm, qb, p, h2, is_b);
   if (__syncthreads_or(st.overflowed())) {
@@ -380,8 +487,9 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_kernel(PrefillArgs a) {
     st.m = exact_row_max(st, ld, lds, kbase, a.c.sp, 0, kv_end, qb, p, h2);
     st.reset();
     ld.load_k(kbase, a.c.sp, 0, kv_end, lds.k0);
-    wait_tile_loads();
-    __syncthreads();
+    load_next_two(ld, lds, kbase, vbase, a.c.sp, kv_end);
+    wait_first_tile();
+    phase_barrier();
     attend_pp<false>(st, ldb, lds, kbase, vbase, a.c.sp, kv_end, n_kt, n_unm, qb, p, h2, is_b);
   }
 

@@ -87,8 +87,10 @@ inline SplitLayout decode_split_layout(int batch, int n_kv, int G, int max_ctx) 
                       decode_keys_per_split(batch, n_kv, rows_before), 1);
 }
 
+// Prefill: the header, then the cos/sin table float2 [total_tokens][64] that
+// the K/V prologue writes for the queries.
 inline size_t prefill_ws_bytes(int total_tokens) {
-  return kWsHeader + round256((size_t)total_tokens * kHalf * 2 * sizeof(float));
+  return kWsHeader + round256((size_t)total_tokens * kHalf * sizeof(float2));
 }
 
 // ---- kernel argument blocks ----------------------------------------------------
@@ -120,7 +122,7 @@ struct PrefillArgs {
   uint16_t* out;
   float* lse;
   int* err;
-  float2* cs;  // cos/sin table in the workspace
+  float2* cs;  // cos/sin table in the workspace, [total_tokens][64]
 };
 
 struct DecodeArgs {

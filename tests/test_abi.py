@@ -143,6 +143,7 @@ def test_verify_validation_paths():
 
 def test_workspace_sizes():
     L = qa.lib()
+    # prefill: header + cos/sin table (64 float2 per token)
     assert L.qa_workspace_bytes(0, 4, 32, 8, 8192, 0) == 256 + 8192 * 512
     d = L.qa_workspace_bytes(1, 4, 32, 8, 2176, 0)
     v = L.qa_workspace_bytes(2, 4, 32, 8, 2064, 16)
