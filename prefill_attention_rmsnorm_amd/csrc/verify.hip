@@ -47,22 +47,47 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(DecodeArgs a, RopeFreq 
   const int p = L0 + ti;
 
   if (k0 < k1) {
-    // ---- new slots owned by this split: k' (fp64) and v into the cache
+    // ---- new slots owned by this split: k' (fp64) and v into the cache.
+    // Wave w takes slots nb0 + w, nb0 + w + NW, ...: all of a round's loads
+    // go out first, and the rotation advances from one slot to the next by
+    // the fp64 angle-addition identity (one turn by NW positions) instead
+    // of a fresh sincos per slot.
     const int nb0 = max(k0, L0), nb1 = min(k1, L0 + n);
-    const double wk0 = a.k_norm_w ? (double)bf_to_f(a.k_norm_w[l]) : 1.0;
-    const double wk1 = a.k_norm_w ? (double)bf_to_f(a.k_norm_w[l + 64]) : 1.0;
-    for (int slot = nb0 + w; slot < nb1; slot += NW) {
-      const int i = slot - L0;
-      double sn, cn;
-      sincos((double)slot * f.inv_freq[l], &sn, &cn);
-      const size_t src = (((size_t)b * n + i) * a.n_kv_heads + g) * kHeadDim;
-      uint16_t o0, o1;
-      kprime_pair(a.k[src + l], a.k[src + l + 64], wk0, wk1, a.eps, cn, sn, &o0, &o1);
-      const size_t crow = (size_t)b * a.c.sb + (size_t)g * a.c.sh + (size_t)slot * a.c.sp;
-      a.c.k[crow + l] = o0;
-      a.c.k[crow + l + 64] = o1;
-      reinterpret_cast<uint32_t*>(a.c.v + crow)[l] =
-          reinterpret_cast<const uint32_t*>(a.v + src)[l];
+    if (nb0 + w < nb1) {  // (wave-uniform)
+      constexpr int CH = 8;  // slots per round and wave
+      const double invf = f.inv_freq[l];
+      const double wk0 = a.k_norm_w ? (double)bf_to_f(a.k_norm_w[l]) : 1.0;
+      const double wk1 = a.k_norm_w ? (double)bf_to_f(a.k_norm_w[l + 64]) : 1.0;
+      double cn, sn, cstep, sstep;
+      sincos((double)(nb0 + w) * invf, &sn, &cn);
+      sincos((double)NW * invf, &sstep, &cstep);
+      for (int base = nb0 + w; base < nb1; base += NW * CH) {
+        uint16_t kx0[CH], kx1[CH];
+        uint32_t vx[CH];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+          const int slot = min(base + NW * c, nb1 - 1);
+          const size_t src = (((size_t)b * n + (slot - L0)) * a.n_kv_heads + g) * kHeadDim;
+          kx0[c] = a.k[src + l];
+          kx1[c] = a.k[src + l + 64];
+          vx[c] = reinterpret_cast<const uint32_t*>(a.v + src)[l];
+        }
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+          const int slot = base + NW * c;
+          if (slot >= nb1) break;  // (wave-uniform)
+          uint16_t o0, o1;
+          kprime_pair(kx0[c], kx1[c], wk0, wk1, a.eps, cn, sn, &o0, &o1);
+          const size_t crow =
+              (size_t)b * a.c.sb + (size_t)g * a.c.sh + (size_t)slot * a.c.sp;
+          a.c.k[crow + l] = o0;
+          a.c.k[crow + l + 64] = o1;
+          reinterpret_cast<uint32_t*>(a.c.v + crow)[l] = vx[c];
+          const double c2 = cn * cstep - sn * sstep;
+          sn = sn * cstep + cn * sstep;
+          cn = c2;
+        }
+      }
     }
 
     // ---- cos/sin of the draft positions for the queries (LDS, fp64
