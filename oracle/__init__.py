@@ -30,6 +30,9 @@ Functions and what pins each of them (tests under ``tests/test_oracle_*``):
                         explicit bottom-right mask, 50-digit brute force
 ``prefill/decode/verify``  causality, decode == prefill row, verify ==
                         sequential decodes, packed == separate, GQA == MHA
+``rmsnorm_hidden``      hand values incl. a tie and the cast-placement case,
+                        constant vectors, torch CPU bf16 add and the
+                        float32 reference arithmetic
 ``lm_logits``           50-digit brute force on tiny shapes
 ``margin_ok``           rule cases (tie, exactly 2.0 below, just over)
 =====================  ====================================================
@@ -59,3 +62,4 @@ from .attention import (  # noqa: F401
     margin_ok,
     argmax_lowest,
 )
+from .rmsnorm_hidden import rmsnorm_hidden  # noqa: F401
