@@ -207,6 +207,97 @@ def cpu_baseline(budget_s=20.0):
                       f"layers"}
 
 
+def ragged_spread(torch, qa, W, reps=15):
+    """Latency of the ragged batch against the length-proportional cost.
+
+    Batch 4 with prompt lengths drawn from {512, 1024, 1536, 2048} (packed
+    prefill, then 64 decode steps at per-sequence contexts) and the same shapes
+    at 2048 tokens each, one layer.  The cost of a prefill is sum S(S+1)
+    (causal pairs), of a decode step the context slots read, sum L.  For each
+    phase ratio = t_ragged / (t_uniform * C_ragged / C_uniform); the check
+    passes when |ratio - 1| <= 0.25.  Prefill times are medians of `reps`
+    calls; a decode step is the mean over 64 graph-replayed steps (median of
+    `reps` replays)."""
+    import numpy as np
+
+    w = W.get(3)
+    B, Hq, Hkv, cap, nsteps = (w.batch, w.n_q_heads, w.n_kv_heads, w.capacity,
+                               w.decode_steps)
+    lens_r = W.ragged_lengths(3, B, w.ragged_choices)
+    lens_u = [max(w.ragged_choices)] * B
+    p = qa.Params(Hq, w.scale, w.theta, w.eps)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+
+    def rnd(*shape):
+        return torch.randn(*shape, generator=g, device="cuda",
+                           dtype=torch.float32).to(torch.bfloat16)
+
+    def measure(lens):
+        T = sum(lens)
+        cu, pos = W.packed_layout(lens)
+        cu, pos = torch.from_numpy(cu).cuda(), torch.from_numpy(pos).cuda()
+        q, k, v = rnd(T, Hq, 128), rnd(T, Hkv, 128), rnd(T, Hkv, 128)
+        cache = qa.Cache.empty(B, Hkv, cap)
+        out = torch.empty((T, Hq, 128), dtype=torch.bfloat16, device="cuda")
+        ws = qa.workspace(qa.QA_OP_PREFILL, B, Hq, Hkv, T)
+        S = max(lens)
+        for _ in range(3):
+            qa.prefill(cache, p, q, k, v, cu, pos, S, out=out, ws=ws)
+        ts = []
+        for _ in range(reps):
+            e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+            e0.record()
+            qa.prefill(cache, p, q, k, v, cu, pos, S, out=out, ws=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        t_pre = float(np.median(ts))
+        dq, dk, dv = rnd(B, Hq, 128), rnd(B, Hkv, 128), rnd(B, Hkv, 128)
+        dpos0 = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        dpos = dpos0.clone()
+        dout = torch.empty((B, Hq, 128), dtype=torch.bfloat16, device="cuda")
+        dws = qa.workspace(qa.QA_OP_DECODE, B, Hq, Hkv, cap)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            qa.decode(cache, p, dq, dk, dv, dpos, cap, out=dout, ws=dws)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(nsteps):
+                qa.decode(cache, p, dq, dk, dv, dpos, cap, out=dout, ws=dws)
+                dpos.add_(1)
+        ts = []
+        for _ in range(reps):
+            dpos.copy_(dpos0)
+            torch.cuda.synchronize()
+            e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+            e0.record()
+            graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3 / nsteps)
+        return t_pre, float(np.median(ts))
+
+    pr, dr = measure(lens_r)
+    pu, du = measure(lens_u)
+    c_pre = sum(x * (x + 1) for x in lens_r) / sum(x * (x + 1) for x in lens_u)
+    c_dec = (sum(lens_r) + B * (nsteps + 1) / 2.0) / \
+        (sum(lens_u) + B * (nsteps + 1) / 2.0)
+
+    def entry(tr, tu, c):
+        ratio = tr / (tu * c)
+        return {"t_ragged_us": round(tr, 2), "t_uniform_us": round(tu, 2),
+                "cost_ratio": round(c, 4), "ratio": round(ratio, 4),
+                "within_25pct": bool(abs(ratio - 1.0) <= 0.25)}
+
+    return {"lengths": lens_r, "uniform_length": lens_u[0],
+            "prefill": entry(pr, pu, c_pre),
+            "decode_step": entry(dr, du, c_dec)}
+
+
 def profile_kernels(wl, torch, qa):
     """One pass of each hot kernel plus a copy of known size, for rocprofv3
     kernel-trace and counter runs: copy 256 MiB x3 (counter calibration),
@@ -374,6 +465,8 @@ def main():
         "wall_s_timed": round(wall, 3),
         "provenance": build_info(),
     }
+    log("bench: ragged-batch latency spread (untimed)")
+    result["ragged_spread"] = ragged_spread(torch, qa, W)
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (fp64 oracle, bounded sample)")
         result["cpu_baseline"] = cpu_baseline()
