@@ -78,6 +78,7 @@ __device__ __forceinline__ void bf16x8_to_f64(u32x4 w, double (&d)[8]) {
 __global__ __launch_bounds__(256) void kv_prologue_kernel(PrefillArgs a,
                                                           RopeFreq f) {
   __shared__ double2 s_cs[4][kHalf];  // per wave: (cos, sin) of the 64 pairs
+  if (blockIdx.x == 0 && threadIdx.x == 0) *a.tile_ctr = 0;  // for the attention grid
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wv;
   if (t >= a.total_tokens) return;
@@ -339,28 +340,21 @@ __device__ __forceinline__ void attend_pp(WaveAttn& st, const TileLoader<4>& ld,
   else pingpong<false, SET_M>(st, ld, lds, kbase, vbase, sp, kend, n_kt, n_unm, qb, lim_abs, h2);
 }
 
-// Blocks are ordered heaviest q-tile first; when the number of (sequence, kv
-// head) pairs is a multiple of 8, all tiles of a pair land on one XCD (the
-// hardware deals workgroup ids to the 8 XCDs round robin), so its K/V stay
-// in that XCD's L2.
+// Work items are q-tiles, numbered heaviest first; when the number of
+// (sequence, kv head) pairs is a multiple of 8, items x and x + 8 belong to
+// pairs of the same residue mod 8.  One q-tile: TQ tokens x G heads of one
+// (sequence, kv head), 256 query rows on 8 waves.
 template <int G>
-__global__ __launch_bounds__(512, 1) void prefill_attn_kernel(PrefillArgs a) {
+__device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int x, const AttnLds& lds,
+                                             unsigned char* lds_cs) {
   constexpr int TQ = 256 / G;            // tokens per workgroup
   constexpr int NPOS = (TQ + 63) / 64;   // positions per lane (each wave reads all)
-  __shared__ __attribute__((aligned(16))) unsigned char lds_k0[kKTileBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char lds_k1[kKTileBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char lds_v0[kKTileBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char lds_v1[kKTileBytes];
   constexpr bool CS_LDS = G >= 4;
-  __shared__ __attribute__((aligned(16))) unsigned char lds_cs[CS_LDS ? TQ * 512 : 16];
-  const AttnLds lds{lds_k0, lds_k1, lds_v0, lds_v1};
-
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = l & 31, h2 = l >> 5;
 
   const int n_pairs = a.n_seq * a.n_kv_heads;
-  const int x = blockIdx.x;
   int pair, qt_rev;
   if ((n_pairs & 7) == 0) {
     const int ppx = n_pairs >> 3, slot = x >> 3;
@@ -513,6 +507,36 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_kernel(PrefillArgs a) {
   }
 }
 
+// Persistent grid, one workgroup per CU: each takes the next q-tile from a
+// counter in the workspace (zeroed by the K/V prologue of the same call)
+// until none is left, so the heaviest tiles start first and every CU stays
+// busy to the end instead of following the hardware's dispatch order.
+template <int G>
+__global__ __launch_bounds__(512, 1) void prefill_attn_kernel(PrefillArgs a) {
+  constexpr int TQ = 256 / G;
+  constexpr bool CS_LDS = G >= 4;
+  __shared__ __attribute__((aligned(16))) unsigned char lds_k0[kKTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_k1[kKTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_v0[kKTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_v1[kKTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_cs[CS_LDS ? TQ * 512 : 16];
+  __shared__ int s_item;
+  const AttnLds lds{lds_k0, lds_k1, lds_v0, lds_v1};
+  const int n_items = a.n_seq * a.n_kv_heads * a.n_qtiles;
+  for (;;) {
+    if (threadIdx.x == 0)
+      s_item = __hip_atomic_fetch_add(a.tile_ctr, 1, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int x = s_item;
+    __syncthreads();  // every wave has its item before s_item is rewritten
+    if (x >= n_items) break;
+    prefill_tile<G>(a, x, lds, lds_cs);
+    wait_tile_loads();  // no copy into LDS outlives the tile
+    __syncthreads();    // nor any LDS read
+  }
+}
+
 hipError_t launch_prefill(const PrefillArgs& a0, const RopeFreq& f, int group,
                           hipStream_t s, int* n_kernels) {
   PrefillArgs a = a0;
@@ -525,7 +549,13 @@ hipError_t launch_prefill(const PrefillArgs& a0, const RopeFreq& f, int group,
   ++*n_kernels;
   const int tq = 256 / group;
   a.n_qtiles = (a.max_seqlen + tq - 1) / tq;
-  const dim3 grid((unsigned)(a.n_seq * a.n_kv_heads * a.n_qtiles));
+  int dev = 0, n_cu = 0;
+  e = hipGetDevice(&dev);
+  if (e == hipSuccess)
+    e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const long n_items = (long)a.n_seq * a.n_kv_heads * a.n_qtiles;
+  const dim3 grid((unsigned)(n_items < n_cu ? n_items : n_cu));
   switch (group) {
     case 1: hipLaunchKernelGGL(prefill_attn_kernel<1>, grid, dim3(512), 0, s, a); break;
     case 2: hipLaunchKernelGGL(prefill_attn_kernel<2>, grid, dim3(512), 0, s, a); break;

@@ -263,6 +263,7 @@ qa_status qa_prefill(const qa_cache* c, const qa_params* p, const void* q,
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
   a.err = static_cast<int*>(ws);
+  a.tile_ctr = static_cast<int*>(ws) + 1;
   a.cs = reinterpret_cast<float2*>(static_cast<char*>(ws) + qa::kWsHeader);
   int nk = 0;
   hipError_t e = qa::launch_prefill(a, make_freq(p->rope_theta), G,

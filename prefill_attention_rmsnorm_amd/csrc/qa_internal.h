@@ -19,7 +19,8 @@ struct RopeFreq {
 };
 
 // ---- workspace layout --------------------------------------------------------
-//   [0, 256)                 int32 error word at 0
+//   [0, 256)                 int32 error word at 0; prefill: int32 q-tile
+//                            counter at 4 (zeroed by every prefill call)
 //   prefill: + cos/sin table float2 [total_tokens][64]
 //   decode / verify: + fp32 m, l [batch][n_kv][n_split][rows] each
 //                    + fp32 o   [batch][n_kv][n_split][rows][128]
@@ -122,6 +123,7 @@ struct PrefillArgs {
   uint16_t* out;
   float* lse;
   int* err;
+  int* tile_ctr;  // q-tile counter of the attention grid (workspace header)
   float2* cs;  // cos/sin table in the workspace, [total_tokens][64]
 };
 

@@ -86,6 +86,16 @@ def test_ragged_contexts():
     run_steps(4, w.n_q_heads, w.n_kv_heads, w.capacity, lens, 3, seed=23)
 
 
+@pytest.mark.parametrize("lens", [[2175, 1, 2, 1000], [0, 2175, 0, 0],
+                                  [5, 2175, 2175, 3]])
+def test_extreme_length_mix(lens):
+    # Cache workgroups are shared out by context length: a near-full context
+    # beside near-empty ones gets most of them (runs still within the split
+    # capacity), and an empty context none.
+    w = W.get(2)
+    run_steps(4, w.n_q_heads, w.n_kv_heads, w.capacity, lens, 1, seed=26)
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 4), (16, 2)])
 def test_groups_and_short_contexts(Hq, Hkv):
     run_steps(3, Hq, Hkv, 200, [0, 1, 130], 3, seed=24)
