@@ -14,6 +14,7 @@ Inputs are synthetic (seeded device draws, bf16 ~N(0,1)) and resident in HBM
 before timing starts.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--no-ragged] [--profile-kernels]
 """
 
 from __future__ import annotations
@@ -330,6 +331,8 @@ def main():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ragged", action="store_true",
+                    help="skip the ragged-batch latency-spread measurement")
     ap.add_argument("--profile-kernels", action="store_true",
                     help="run each hot kernel once (for rocprofv3) and exit")
     args = ap.parse_args()
@@ -465,8 +468,9 @@ def main():
         "wall_s_timed": round(wall, 3),
         "provenance": build_info(),
     }
-    log("bench: ragged-batch latency spread (untimed)")
-    result["ragged_spread"] = ragged_spread(torch, qa, W)
+    if not args.no_ragged:
+        log("bench: ragged-batch latency spread (untimed)")
+        result["ragged_spread"] = ragged_spread(torch, qa, W)
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (fp64 oracle, bounded sample)")
         result["cpu_baseline"] = cpu_baseline()
