@@ -299,6 +299,39 @@ def ragged_spread(torch, qa, W, reps=15):
             "decode_step": entry(dr, du, c_dec)}
 
 
+def rmsnorm_rate(torch, qa, reps=20):
+    """qa_rmsnorm_hidden at the prefill shape of the workload: 4 x 2048
+    tokens of hidden 2560, with the residual add and a weight.  Algorithmic
+    bytes per call: x and residual read, out and residual written (the 5 KB
+    weight aside), 4 * T * H * 2.  Median of `reps` event-timed calls."""
+    import numpy as np
+
+    T, H = 4 * 2048, 2560
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4)
+    x = torch.randn(T, H, generator=g, device="cuda").to(torch.bfloat16)
+    res = torch.randn(T, H, generator=g, device="cuda").to(torch.bfloat16)
+    w = (1.0 + 0.1 * torch.randn(H, generator=g, device="cuda")).to(
+        torch.bfloat16)
+    out = torch.empty_like(x)
+    for _ in range(3):
+        qa.rmsnorm_hidden(x, residual=res, weight=w, out=out)
+    ts = []
+    for _ in range(reps):
+        e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+        e0.record()
+        qa.rmsnorm_hidden(x, residual=res, weight=w, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    us = float(np.median(ts))
+    nbytes = 4 * T * H * 2
+    gbps = nbytes / (us * 1e-6) / 1e9
+    return {"tokens": T, "hidden": H, "us": round(us, 2),
+            "algorithmic_bytes": nbytes, "GBps": round(gbps, 1),
+            "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
 def profile_kernels(wl, torch, qa):
     """One pass of each hot kernel plus a copy of known size, for rocprofv3
     kernel-trace and counter runs: copy 256 MiB x3 (counter calibration),
@@ -332,7 +365,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ragged", action="store_true",
-                    help="skip the ragged-batch latency-spread measurement")
+                    help="skip the untimed extras (ragged-batch latency spread, "
+                         "hidden-state RMSNorm rate)")
     ap.add_argument("--profile-kernels", action="store_true",
                     help="run each hot kernel once (for rocprofv3) and exit")
     args = ap.parse_args()
@@ -471,6 +505,8 @@ def main():
     if not args.no_ragged:
         log("bench: ragged-batch latency spread (untimed)")
         result["ragged_spread"] = ragged_spread(torch, qa, W)
+        log("bench: hidden-state RMSNorm (untimed)")
+        result["rmsnorm_hidden"] = rmsnorm_rate(torch, qa)
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (fp64 oracle, bounded sample)")
         result["cpu_baseline"] = cpu_baseline()

@@ -202,7 +202,26 @@ qa_status qa_verify(const qa_cache* c, const qa_params* p, const void* q,
                     int batch, int block_len, int max_ctx, void* out,
                     float* lse, void* ws, size_t ws_bytes, void* stream);
 
-/* Plain device copy of `bytes` (multiple of 16) from src to dst on `stream`;
+/*
+ * Hidden-state RMSNorm with the residual add, in the reference model's cast
+ * placement ("dryft-flash-infer" agent guide, Where the wins are: RMSNorm is
+ * small, repeated and safe to fuse; Numerics: reductions may be reordered, the
+ * bf16 cast may not move).  For each of n_tokens rows of `hidden` values:
+ *   r   = bf16(x + residual)               (r = x when residual is NULL)
+ *   out = bf16(weight * bf16(r / sqrt(mean(r^2) + eps)))   (weight NULL = 1)
+ * and residual, when given, is overwritten with r (the updated residual
+ * stream).  Every step other than the three bf16 roundings is exact up to the
+ * order of the sum of squares.
+ *   x, residual, out bf16 [n_tokens][hidden] (dense), weight bf16 [hidden]
+ *   hidden a multiple of 8, at most 8192; out may not alias x or residual
+ * n_tokens == 0 is a valid no-op (the pointers may then be NULL).
+ * Asynchronous on `stream`, allocates nothing.
+ */
+qa_status qa_rmsnorm_hidden(const void* x, void* residual, const void* weight,
+                            int n_tokens, int hidden, double eps, void* out,
+                            void* stream);
+
+/* Plain device copy of `bytes` (multiple of 16) from src to dst on `stream`;/* Plain device copy of `bytes` (multiple of 16) from src to dst on `stream`;
  * the calibration kernel for bandwidth and traffic measurements. */
 qa_status qa_copy(const void* src, void* dst, size_t bytes, void* stream);
 

@@ -23,8 +23,8 @@ LIB = os.path.join(PKG, "libqa.so")
 ARCH = "gfx950"
 
 SOURCES = ["qa_api.cpp", "util.hip", "prefill.hip", "decode.hip", "verify.hip",
-           "merge.hip"]
-HEADERS = ["qa_internal.h", "qa_device.h", "attn_tile.h"]
+           "merge.hip", "rmsnorm.hip"]
+HEADERS = ["qa_internal.h", "qa_device.h", "attn_tile.h", "rmsnorm.h"]
 
 
 def hipcc() -> str:

@@ -13,6 +13,7 @@
 
 #include "qa.h"
 #include "qa_internal.h"
+#include "rmsnorm.h"
 
 namespace {
 
@@ -376,6 +377,33 @@ qa_status qa_verify(const qa_cache* c, const qa_params* p, const void* q,
   g_counters[CNT_KERNELS].fetch_add(nk);
   if (e != hipSuccess) return hip_fail(e, "verify launch");
   g_counters[CNT_VERIFY].fetch_add(1);
+  g_last_error.clear();
+  return QA_OK;
+}
+
+qa_status qa_rmsnorm_hidden(const void* x, void* residual, const void* weight,
+                            int n_tokens, int hidden, double eps, void* out,
+                            void* stream) {
+  QA_REQUIRE((x && out) || n_tokens == 0, QA_ERR_NULL, "x and out must be non-NULL");
+  QA_REQUIRE(n_tokens >= 0, QA_ERR_SHAPE, "n_tokens %d < 0", n_tokens);
+  QA_REQUIRE(hidden >= 8 && hidden % 8 == 0, QA_ERR_SHAPE,
+             "hidden %d must be a positive multiple of 8", hidden);
+  QA_REQUIRE(hidden <= 64 * 8 * qa::kNormMaxChunks, QA_ERR_UNSUPPORTED,
+             "hidden %d exceeds %d", hidden, 64 * 8 * qa::kNormMaxChunks);
+  QA_REQUIRE(eps >= 0.0 && eps < 1.0e30, QA_ERR_SHAPE, "eps must be finite and >= 0");
+  QA_REQUIRE(al16(x) && al16(out) && al16(residual) && al16(weight), QA_ERR_ALIGN,
+             "x/residual/weight/out must be 16-byte aligned");
+  qa::NormArgs a;
+  a.x = static_cast<const uint16_t*>(x);
+  a.res = static_cast<uint16_t*>(residual);
+  a.w = static_cast<const uint16_t*>(weight);
+  a.out = static_cast<uint16_t*>(out);
+  a.n_tokens = n_tokens;
+  a.hidden = hidden;
+  a.eps = eps;
+  hipError_t e = qa::launch_rmsnorm_hidden(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");
+  if (n_tokens > 0) g_counters[CNT_KERNELS].fetch_add(1);
   g_last_error.clear();
   return QA_OK;
 }

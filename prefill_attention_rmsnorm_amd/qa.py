@@ -23,6 +23,7 @@ HEAD_DIM = 128
 EXPORTS = (
     "qa_cache_alloc", "qa_cache_free", "qa_workspace_bytes",
     "qa_workspace_init", "qa_prefill", "qa_decode", "qa_verify", "qa_copy",
+    "qa_rmsnorm_hidden",
     "qa_status_str", "qa_last_error", "qa_get_counters", "qa_reset_counters",
     "qa_device_error",
 )
@@ -82,6 +83,8 @@ def lib():
         "qa_verify": (_i32, [P(QaCache), P(QaParams), _vp, _vp, _vp, _vp,
                              _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
         "qa_copy": (_i32, [_vp, _vp, _sz, _vp]),
+        "qa_rmsnorm_hidden": (_i32, [_vp, _vp, _vp, _i32, _i32, ctypes.c_double,
+                                     _vp, _vp]),
         "qa_status_str": (ctypes.c_char_p, [_i32]),
         "qa_last_error": (ctypes.c_char_p, []),
         "qa_get_counters": (None, [P(ctypes.c_uint64)]),
@@ -299,6 +302,29 @@ def copy(src: torch.Tensor, dst: torch.Tensor, stream=None):
     if dst.numel() * dst.element_size() < nbytes:
         raise ValueError("dst smaller than src")
     _check(lib().qa_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
+
+
+def rmsnorm_hidden(x, residual=None, weight=None, eps=1e-6, out=None,
+                   stream=None):
+    """qa_rmsnorm_hidden on x bf16 [T, H]; residual (bf16 [T, H], updated in
+    place with bf16(x + residual)) and weight (bf16 [H]) are optional.
+    Returns out."""
+    if x.dim() != 2:
+        raise ValueError("x must be [n_tokens, hidden]")
+    T, H = x.shape
+    _need(x, "x", torch.bfloat16, T * H)
+    if residual is not None:
+        _need(residual, "residual", torch.bfloat16, T * H)
+    if weight is not None:
+        _need(weight, "weight", torch.bfloat16, H)
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", torch.bfloat16, T * H)
+    _check(lib().qa_rmsnorm_hidden(
+        _ptr(x), None if residual is None else _ptr(residual),
+        None if weight is None else _ptr(weight), T, H, float(eps), _ptr(out),
+        _stream(stream)))
+    return out
 
 
 def device_error(ws: torch.Tensor, stream=None) -> int:

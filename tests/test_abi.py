@@ -150,3 +150,28 @@ def test_workspace_sizes():
     assert d > 0 and v > d
     assert L.qa_workspace_bytes(1, 4, 32, 7, 2176, 0) == 0   # bad group
     assert L.qa_workspace_bytes(2, 4, 32, 8, 2064, 64) == 0  # 256 rows
+
+
+def _norm(x=FAKE, res=None, w=None, T=4, H=2560, eps=1e-6, out=FAKE * 3):
+    return qa.lib().qa_rmsnorm_hidden(x, res, w, T, H, eps, out, None)
+
+
+def test_rmsnorm_hidden_validation_paths():
+    before = qa.counters()
+    assert _norm(x=None) == -1
+    assert _norm(out=None) == -1
+    assert _norm(T=-1) == -2
+    assert _norm(H=0) == -2
+    assert _norm(H=2564) == -2                       # not a multiple of 8
+    assert _norm(H=8200) == -3                       # more than 8192
+    assert _norm(eps=-1.0) == -2
+    assert _norm(eps=float("nan")) == -2
+    assert _norm(x=FAKE + 8) == -4                   # alignment
+    assert _norm(res=FAKE * 5 + 4) == -4
+    assert _norm(w=FAKE * 7 + 2) == -4
+    assert b"aligned" in qa.lib().qa_last_error()
+    assert qa.counters()[4] - before[4] == 11
+    assert qa.counters()[3] == before[3]             # nothing launched
+    assert _norm(T=0) == 0                           # empty call: a no-op
+    assert _norm(x=None, out=None, T=0) == 0         # (any pointers)
+    assert qa.counters()[3] == before[3]

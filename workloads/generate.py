@@ -15,7 +15,7 @@ import torch
 TAG = {
     "q": 1, "k": 2, "v": 3, "cache_k": 4, "cache_v": 5, "emb": 6,
     "w_q": 7, "w_k": 8, "w_v": 9, "w_o": 10, "w_lm": 11, "ids": 12,
-    "lens": 13, "norm_w": 14,
+    "lens": 13, "norm_w": 14, "hidden_x": 15, "hidden_res": 16,
 }
 
 
