@@ -118,3 +118,35 @@ def check_cache(cache: qa.Cache, ocache: oracle.Cache, what="cache"):
 
 def seq_index(lens):
     return np.repeat(np.arange(len(lens)), lens)
+
+
+class LMHead:
+    """Test-side LM head over the attention output (W_o [Hq*128, hidden], a
+    final RMSNorm, W_lm [hidden, vocab], all random-init ~N(0, 0.02)): an fp32
+    torch version on the GPU for the engine and the fp64 oracle version for
+    the replay."""
+
+    def __init__(self, widx, n_q_heads, hidden, vocab):
+        say(f"LM head: W_o [{n_q_heads * 128}, {hidden}], W_lm [{hidden}, {vocab}]")
+        self.w_o = W.normal_bf16((n_q_heads * 128, hidden), widx, 0, 0, "w_o",
+                                 std=0.02)
+        self.w_lm = W.normal_bf16((hidden, vocab), widx, 0, 0, "w_lm",
+                                  std=0.02)
+        self.w_o_np = self.w_o.double().numpy()
+        self.w_lm_np = self.w_lm.float().numpy()
+        self.w_o_gpu = self.w_o.float().cuda()
+        self.w_lm_gpu = self.w_lm.float().cuda()
+
+    def gpu_logits(self, o_gpu):
+        """Engine side: the fp32 LM head on the GPU attention output."""
+        h = o_gpu.reshape(o_gpu.shape[0], -1).float() @ self.w_o_gpu
+        h = h * torch.rsqrt(h.pow(2).mean(-1, keepdim=True) + EPS)
+        return h @ self.w_lm_gpu
+
+    def gpu_tokens(self, o_gpu):
+        """Engine side: argmax of the fp32 LM head on the GPU output."""
+        return self.gpu_logits(o_gpu).argmax(-1).cpu().numpy()
+
+    def ref_logits(self, o_ref):
+        return oracle.lm_logits(o_ref.reshape(o_ref.shape[0], -1), self.w_o_np,
+                                self.w_lm_np, EPS)

@@ -18,35 +18,11 @@ import oracle
 import workloads as W
 from prefill_attention_rmsnorm_amd import qa
 
-from .gpu_helpers import EPS, THETA, f64, new_cache, params, say
+from .gpu_helpers import EPS, THETA, LMHead, f64, new_cache, params, say
 
 pytestmark = pytest.mark.gpu
 SCALE = 1.0 / np.sqrt(128)
 MARGIN = 2.0
-
-
-class LMHead:
-    def __init__(self, widx, n_q_heads, hidden, vocab):
-        say(f"LM head: W_o [{n_q_heads * 128}, {hidden}], W_lm [{hidden}, {vocab}]")
-        self.w_o = W.normal_bf16((n_q_heads * 128, hidden), widx, 0, 0, "w_o",
-                                 std=0.02)
-        self.w_lm = W.normal_bf16((hidden, vocab), widx, 0, 0, "w_lm",
-                                  std=0.02)
-        self.w_o_np = self.w_o.double().numpy()
-        self.w_lm_np = self.w_lm.float().numpy()
-        self.w_o_gpu = self.w_o.float().cuda()
-        self.w_lm_gpu = self.w_lm.float().cuda()
-
-    def gpu_tokens(self, o_gpu):
-        """Engine side: argmax of the fp32 LM head on the GPU output."""
-        h = o_gpu.reshape(o_gpu.shape[0], -1).float() @ self.w_o_gpu
-        h = h * torch.rsqrt(h.pow(2).mean(-1, keepdim=True) + EPS)
-        logits = h @ self.w_lm_gpu
-        return logits.argmax(-1).cpu().numpy()
-
-    def ref_logits(self, o_ref):
-        return oracle.lm_logits(o_ref.reshape(o_ref.shape[0], -1), self.w_o_np,
-                                self.w_lm_np, EPS)
 
 
 def _judge(logits_ref, toks, what):

@@ -1,0 +1,185 @@
+"""Exact speculative decoding on the GPU: the host loop over qa_verify emits
+the same tokens as plain greedy decoding with qa_decode, whatever the drafter
+proposes ("dryft-flash-infer" agent guide, Where the wins are: speculative
+decoding with exact verification).
+
+Model around the attention (test plumbing, as in the greedy check): the tiny
+workload's embedding and q/k/v projections (hidden 2560, 4 query heads, one
+KV head) and a random-init LM head (W_o, final RMSNorm, W_lm over 151936
+tokens).  Two sequences with prompts of 64 and 37 tokens, 24 new tokens each,
+blocks of 4 (three draft tokens per step).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from prefill_attention_rmsnorm_amd import qa, specdec
+
+from .gpu_helpers import LMHead, bits, new_cache, params, say
+
+pytestmark = pytest.mark.gpu
+N_NEW, BLOCK, LENS = 24, 4, (64, 37)
+TIE = 1e-2  # logits closer than this may order differently between kernels
+
+
+class Model:
+    def __init__(self):
+        w = W.get("tiny")
+        self.Hq, self.Hkv, self.D, self.V = (w.n_q_heads, w.n_kv_heads,
+                                             w.hidden, w.vocab)
+        self.emb = W.normal_bf16((self.V, self.D), 0, 0, 0, "emb")
+        # fp64 on the host, then one bf16 rounding: a token's q/k/v do not
+        # depend on how many rows are projected together (a GPU GEMM's
+        # summation order can), so both runs feed identical inputs
+        self.w_q = W.normal_bf16((self.D, self.Hq * 128), 0, 0, 0, "w_q",
+                                 std=0.02).double()
+        self.w_k = W.normal_bf16((self.D, self.Hkv * 128), 0, 0, 0, "w_k",
+                                 std=0.02).double()
+        self.w_v = W.normal_bf16((self.D, self.Hkv * 128), 0, 0, 0, "w_v",
+                                 std=0.02).double()
+        self.head = LMHead(0, self.Hq, self.D, self.V)
+        self.p = params(self.Hq)
+        self.cap = max(LENS) + N_NEW + 2 * BLOCK
+
+    def project(self, toks):
+        """q, k, v bf16 [B, n, H, 128] for tokens [B][n]."""
+        t = torch.as_tensor(np.asarray(toks, dtype=np.int64))
+        h = self.emb[t.reshape(-1)].double()
+        B, n = t.shape
+
+        def proj(w, H):
+            return (h @ w).to(torch.bfloat16).reshape(B, n, H, 128).cuda()
+        return proj(self.w_q, self.Hq), proj(self.w_k, self.Hkv), \
+            proj(self.w_v, self.Hkv)
+
+    def prefill(self, prompts):
+        cache = new_cache(len(prompts), self.Hkv, self.cap)
+        lens = [len(x) for x in prompts]
+        flat = [[t] for x in prompts for t in x]
+        q, k, v = self.project(flat)
+        T = len(flat)
+        cu, pos = W.packed_layout(lens)
+        out, _, _ = qa.prefill(cache, self.p, q.reshape(T, self.Hq, 128),
+                               k.reshape(T, self.Hkv, 128),
+                               v.reshape(T, self.Hkv, 128),
+                               torch.from_numpy(cu).cuda(),
+                               torch.from_numpy(pos).cuda(), max(lens))
+        last = torch.from_numpy(cu[1:] - 1).long().cuda()
+        first = self.head.gpu_tokens(out[last])
+        return cache, [int(x) for x in first]
+
+
+@pytest.fixture(scope="module")
+def model():
+    return Model()
+
+
+@pytest.fixture(scope="module")
+def prompts(model):
+    g = W.rng(0, 0, 1, "ids")
+    return [list(map(int, g.integers(0, model.V, n))) for n in LENS]
+
+
+@pytest.fixture(scope="module")
+def greedy(model, prompts):
+    """Plain greedy decoding with qa_decode; tokens and per-step logits."""
+    cache, nxt = model.prefill(prompts)
+    B = len(prompts)
+    toks = [[t] for t in nxt]
+    logits = []
+    pos = np.array(LENS, dtype=np.int32)
+    ws = qa.workspace(qa.QA_OP_DECODE, B, model.Hq, model.Hkv, model.cap)
+    for _ in range(N_NEW - 1):
+        q, k, v = model.project([[t[-1]] for t in toks])
+        out, _, _ = qa.decode(cache, model.p, q[:, 0], k[:, 0], v[:, 0],
+                              torch.from_numpy(pos).cuda(), model.cap, ws=ws)
+        lg = model.head.gpu_logits(out)
+        logits.append(lg.cpu())
+        for b, t in enumerate(lg.argmax(-1).cpu().numpy()):
+            toks[b].append(int(t))
+        pos = pos + 1
+    say(f"greedy tokens: {[t[:8] for t in toks]}")
+    return toks, logits, cache
+
+
+def _agree(spec, greedy_toks, logits, what):
+    """Spec tokens equal the greedy ones; a difference is allowed only at a
+    near-tie of the greedy run's logits (two kernels, two summation orders),
+    after which the sequences are no longer comparable.  Returns, per
+    sequence, the index of the first difference (N_NEW if none)."""
+    first = []
+    for b, (s, g) in enumerate(zip(spec, greedy_toks)):
+        first.append(N_NEW)
+        for i, (ts, tg) in enumerate(zip(s, g)):
+            if ts == tg:
+                continue
+            assert i > 0, f"{what}: first token differs"
+            lg = logits[i - 1][b]
+            gap = float(lg[tg] - lg[ts])
+            say(f"  {what}: seq {b} token {i}: {ts} vs {tg}, gap {gap:.2e}")
+            assert gap <= TIE, f"{what}: seq {b} token {i} differs by {gap}"
+            first[-1] = i
+            break
+    return first
+
+
+def _run(model, prompts, drafter, what):
+    cache, nxt = model.prefill(prompts)
+    lengths = list(LENS)
+    calls = []
+
+    def argmax(o):
+        calls.append(1)
+        return model.head.gpu_tokens(o)
+    spec = specdec.speculative_generate(cache, model.p, model.project, argmax,
+                                        drafter, lengths, nxt, N_NEW, BLOCK,
+                                        model.cap)
+    say(f"  {what}: {len(calls)} verify calls for {N_NEW} tokens")
+    return spec, lengths, cache, len(calls)
+
+
+def test_perfect_drafter_accepts_whole_blocks(model, prompts, greedy):
+    toks, logits, gcache = greedy
+
+    def drafter(b, emitted, k):  # the greedy continuation itself
+        i = len(emitted) + 1
+        return (toks[b][i:i + k] + [0] * k)[:k]
+    spec, lengths, cache, calls = _run(model, prompts, drafter, "perfect")
+    first = _agree(spec, toks, logits, "perfect")
+    # whole blocks accepted up to a near-tie divergence (if any), one token
+    # per call after it at worst
+    i0 = min(first)
+    assert calls <= -(-i0 // BLOCK) + (N_NEW - i0) + 1
+    # the slots of the tokens both runs share hold the same K/V bytes
+    for b, L in enumerate(LENS):
+        n = L + min(first[b], N_NEW - 1)
+        assert np.array_equal(bits(cache.k[b, :, :n]), bits(gcache.k[b, :, :n]))
+        assert np.array_equal(bits(cache.v[b, :, :n]), bits(gcache.v[b, :, :n]))
+
+
+def test_random_drafter_still_exact(model, prompts, greedy):
+    toks, logits, _ = greedy
+    g = np.random.default_rng(70)
+
+    def drafter(b, emitted, k):
+        return list(map(int, g.integers(0, model.V, k)))
+    spec, _, _, calls = _run(model, prompts, drafter, "random")
+    _agree(spec, toks, logits, "random")
+    assert calls >= N_NEW - 1  # (nothing accepted beyond the target's token)
+
+
+def test_partly_right_drafter(model, prompts, greedy):
+    toks, logits, _ = greedy
+    g = np.random.default_rng(71)
+
+    def drafter(b, emitted, k):  # right up to a random point, then wrong
+        i = len(emitted) + 1
+        d = (toks[b][i:i + k] + [0] * k)[:k]
+        cut = int(g.integers(0, k + 1))
+        return d[:cut] + [(t + 1) % model.V for t in d[cut:]]
+    spec, lengths, _, _ = _run(model, prompts, drafter, "partly right")
+    _agree(spec, toks, logits, "partly right")
+    assert all(l0 + N_NEW <= L < l0 + N_NEW + BLOCK
+               for L, l0 in zip(lengths, LENS))
