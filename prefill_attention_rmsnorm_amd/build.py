@@ -24,7 +24,8 @@ ARCH = "gfx950"
 
 SOURCES = ["qa_api.cpp", "util.hip", "prefill.hip", "decode.hip", "verify.hip",
            "merge.hip", "rmsnorm.hip"]
-HEADERS = ["qa_internal.h", "qa_device.h", "attn_tile.h", "rmsnorm.h"]
+HEADERS = ["qa_internal.h", "qa_device.h", "attn_tile.h", "rmsnorm.h",
+           "verify_layout.h"]
 
 
 def hipcc() -> str:
@@ -85,7 +86,7 @@ def _write_build_info():
         "prefill_source_sha": _sha(["prefill.hip", "attn_tile.h",
                                     "qa_device.h", "qa_internal.h"]),
         "verify_source_sha": _sha(["verify.hip", "attn_tile.h", "qa_device.h",
-                                   "qa_internal.h"]),
+                                   "qa_internal.h", "verify_layout.h"]),
     }
     with open(os.path.join(BUILD, "BUILD_INFO.json"), "w") as f:
         json.dump(info, f, indent=1)

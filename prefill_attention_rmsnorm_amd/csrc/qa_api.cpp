@@ -14,6 +14,7 @@
 #include "qa.h"
 #include "qa_internal.h"
 #include "rmsnorm.h"
+#include "verify_layout.h"
 
 namespace {
 
@@ -185,9 +186,7 @@ size_t qa_workspace_bytes(int op, int batch, int n_q_heads, int n_kv_heads,
       return qa::decode_split_layout(batch, n_kv_heads, G, max_ctx).total;
     case QA_OP_VERIFY:
       if (max_ctx < 1 || block_len < 1 || block_len * G > 128) return 0;
-      return qa::split_layout(batch, n_kv_heads, block_len * G, max_ctx,
-                              qa::verify_keys_per_split(batch, n_kv_heads, max_ctx))
-          .total;
+      return qa::verify_split_layout(batch, n_kv_heads, G, max_ctx, block_len).total;
     default:
       return 0;
   }
@@ -363,9 +362,8 @@ qa_status qa_verify(const qa_cache* c, const qa_params* p, const void* q,
   QA_REQUIRE(al16(q) && al16(k) && al16(v) && al16(out) && al16(ws) && al4(lse) &&
                  al4(start_pos),
              QA_ERR_ALIGN, "q/k/v/out/ws must be 16-byte aligned");
-  const qa::SplitLayout L = qa::split_layout(
-      batch, c->n_kv_heads, block_len * G, max_ctx,
-      qa::verify_keys_per_split(batch, c->n_kv_heads, max_ctx));
+  const qa::SplitLayout L =
+      qa::verify_split_layout(batch, c->n_kv_heads, G, max_ctx, block_len);
   QA_REQUIRE(ws_bytes >= L.total, QA_ERR_WORKSPACE,
              "workspace %zu bytes < %zu needed", ws_bytes, L.total);
   qa::DecodeArgs a;

@@ -54,15 +54,6 @@ inline int decode_keys_per_split(int batch, int n_kv, int max_ctx) {
   return (int)ks;
 }
 
-// Verify: about one workgroup per CU in total; splits are whole 64-key tiles.
-inline int verify_keys_per_split(int batch, int n_kv, int max_ctx) {
-  long pairs = (long)batch * n_kv;
-  long want = pairs >= 256 ? 1 : 256 / pairs;  // splits per (sequence, kv head)
-  long ks = (max_ctx + want - 1) / want;
-  ks = (ks + kKeyTile - 1) / kKeyTile * kKeyTile;
-  return ks < kKeyTile ? kKeyTile : (int)ks;
-}
-
 // extra: partials beyond the cache splits (decode adds one for the new token).
 inline SplitLayout split_layout(int batch, int n_kv, int rows, int max_ctx,
                                 int keys_per_split, int extra = 0) {

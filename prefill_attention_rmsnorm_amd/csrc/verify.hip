@@ -8,9 +8,13 @@
 // are split across workgroups, each writing a partial that merge.hip
 // combines in split order.
 //
-// The workgroup whose key range holds some of the new slots first runs the
-// prologue for them (k' in fp64 with one RNE) and writes them to the cache;
-// only that workgroup ever reads those slots in this call, and the block
+// Splits 0 .. n_split-2 take near-equal runs of whole 64-key tiles of the
+// slots before the block (cut on the device from the start position, so the
+// grid depends on the launch sizes only); split n_split-1 runs the prologue
+// for the block's own slots (k' in fp64 with one RNE), writes them to the
+// cache and attends to them alone, so the prologue, the longest part of any
+// workgroup's start, is not followed by a long run of cache tiles.  Only
+// that workgroup ever reads the block's slots in this call, and the block
 // barrier orders its own writes before its reads.
 #include "attn_tile.h"
 #include "qa.h"
@@ -30,13 +34,23 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(DecodeArgs a, RopeFreq 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int j = l & 31, h2 = l >> 5;
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int n = a.block_len, KS = a.keys_per_split;
+  const int n = a.block_len;
   const int rows = n * G;
   const int L0 = a.positions[b];
   const bool ok = L0 >= 0 && L0 + n <= a.max_ctx;
   if (!ok && split == 0 && g == 0 && tid == 0) flag_error(a.err, QA_DEVERR_POSITION);
-  const int kv_end = ok ? L0 + n : 0;
-  const int k0 = split * KS, k1 = min(k0 + KS, kv_end);
+  const int n_old = a.n_split - 1;
+  int k0, k1;
+  if (split < n_old) {  // tiles t0 .. t1-1 of the slots before the block
+    const int nt = ok ? (L0 + kKeyTile - 1) / kKeyTile : 0;
+    const int t0 = (int)((long)split * nt / n_old);
+    const int t1 = (int)((long)(split + 1) * nt / n_old);
+    k0 = t0 * kKeyTile;
+    k1 = ok ? min(t1 * kKeyTile, L0) : 0;
+  } else {  // the block's own slots
+    k0 = ok ? L0 : 0;
+    k1 = ok ? L0 + n : 0;
+  }
   const size_t pairidx = (size_t)b * a.n_kv_heads + g;
   const size_t rowbase = (pairidx * a.n_split + split) * rows;
 
@@ -72,12 +86,38 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(DecodeArgs a, RopeFreq 
           kx1[c] = a.k[src + l + 64];
           vx[c] = reinterpret_cast<const uint32_t*>(a.v + src)[l];
         }
+        // The slots' sums of squares are reduced across the wave together,
+        // one butterfly step for all of them at a time, so their shuffle
+        // latencies overlap (one slot after the other, the chains made this
+        // workgroup the last of the launch).  Per slot the arithmetic is
+        // kprime_pair's: the same products and sums in the same order.
+        double ss[CH];
+        {
+#pragma clang fp contract(off)
+#pragma unroll
+          for (int c = 0; c < CH; ++c) {
+            const double x0 = (double)bf_to_f(kx0[c]), x1 = (double)bf_to_f(kx1[c]);
+            ss[c] = x0 * x0 + x1 * x1;
+          }
+#pragma unroll
+          for (int o = 32; o >= 1; o >>= 1)
+#pragma unroll
+            for (int c = 0; c < CH; ++c) ss[c] += __shfl_xor(ss[c], o);
+        }
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
           const int slot = base + NW * c;
           if (slot >= nb1) break;  // (wave-uniform)
           uint16_t o0, o1;
-          kprime_pair(kx0[c], kx1[c], wk0, wk1, a.eps, cn, sn, &o0, &o1);
+          {
+#pragma clang fp contract(off)
+            const double x0 = (double)bf_to_f(kx0[c]), x1 = (double)bf_to_f(kx1[c]);
+            const double r = sqrt(ss[c] / 128.0 + a.eps);
+            const double y0 = x0 / r * wk0;
+            const double y1 = x1 / r * wk1;
+            o0 = f64_to_bf16_rne(y0 * cn - y1 * sn);
+            o1 = f64_to_bf16_rne(y1 * cn + y0 * sn);
+          }
           const size_t crow =
               (size_t)b * a.c.sb + (size_t)g * a.c.sh + (size_t)slot * a.c.sp;
           a.c.k[crow + l] = o0;
