@@ -221,7 +221,7 @@ qa_status qa_rmsnorm_hidden(const void* x, void* residual, const void* weight,
                             int n_tokens, int hidden, double eps, void* out,
                             void* stream);
 
-/* Plain device copy of `bytes` (multiple of 16) from src to dst on `stream`;/* Plain device copy of `bytes` (multiple of 16) from src to dst on `stream`;
+/* Plain device copy of `bytes` (multiple of 16) from src to dst on `stream`;
  * the calibration kernel for bandwidth and traffic measurements. */
 qa_status qa_copy(const void* src, void* dst, size_t bytes, void* stream);
 
