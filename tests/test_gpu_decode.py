@@ -96,6 +96,14 @@ def test_extreme_length_mix(lens):
     run_steps(4, w.n_q_heads, w.n_kv_heads, w.capacity, lens, 1, seed=26)
 
 
+def test_large_batch_one_split_per_pair():
+    # 64 sequences x 8 kv heads: 512 (sequence, kv head) pairs, so the split
+    # layout falls to its floor (one cache split of up to 16 tiles per pair)
+    g = np.random.default_rng(27)
+    lens = [int(x) for x in g.integers(0, 250, 64)]
+    run_steps(64, 32, 8, 260, lens, 2, seed=27)
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 4), (16, 2)])
 def test_groups_and_short_contexts(Hq, Hkv):
     run_steps(3, Hq, Hkv, 200, [0, 1, 130], 3, seed=24)

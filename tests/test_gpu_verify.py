@@ -58,6 +58,14 @@ def test_shapes(Hq, Hkv, n):
     run_verify(2, Hq, Hkv, 300, [100, 7], n, seed=42)
 
 
+def test_large_batch_one_old_split():
+    # 32 sequences x 8 kv heads: 256 pairs, one old-slot split per pair (plus
+    # the block's own workgroup); starts from 0 (no old slots) upward
+    g = np.random.default_rng(43)
+    starts = [0, 1, 63, 64] + [int(x) for x in g.integers(0, 300, 28)]
+    run_verify(32, 32, 8, 320, starts, 8, seed=43)
+
+
 def test_verify_equals_sequential_decodes():
     B, Hq, Hkv, cap, n, L = 2, 32, 8, 600, 16, 500
     cache_v = new_cache(B, Hkv, cap)
