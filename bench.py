@@ -435,8 +435,9 @@ def main():
     pflops = prefill_flops(B, Hq, S)
     pre_tflops = pflops * L / (pre_ms * 1e-3) / 1e12
 
-    # Live per-call durations from the timed region: a decode call is
-    # decode_kernel + merge_kernel; inside the captured step graph the calls
+    # Live per-call durations from the timed region: a decode call is one
+    # decode_kernel launch (B x Hkv = 32 pairs: partials merged inside it);
+    # inside the captured step graph the calls
     # run back to back, so the phase time over (steps x layers) calls is the
     # average duration of one call on its stream (the position increment, one
     # tiny kernel per step, is included).
@@ -482,8 +483,8 @@ def main():
         "prefill_TFLOPs": round(pre_tflops, 1),
         "prefill_frac_mfma_peak": round(pre_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "verify_us": round(ver_us, 2),
-        "roofline": {"kernel": "qa_decode call = decode_kernel<4,9> + "
-                               "merge_kernel", "bound": "hbm",
+        "roofline": {"kernel": "qa_decode call = decode_kernel<4,9> "
+                               "(one launch, merge inside)", "bound": "hbm",
                      "achieved": round(dec_ach, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s",
                      "frac": round(dec_ach / HBM_PEAK_GBPS, 4),

@@ -69,8 +69,12 @@ enum { QA_OP_PREFILL = 0, QA_OP_DECODE = 1, QA_OP_VERIFY = 2 };
 /* Device-side error bits (qa_device_error). */
 enum {
   QA_DEVERR_POSITION = 1, /* a position outside the cache or the context */
-  QA_DEVERR_SEQLENS = 2   /* cu_seqlens not increasing from 0 to total_tokens,
+  QA_DEVERR_SEQLENS = 2,  /* cu_seqlens not increasing from 0 to total_tokens,
                              or a sequence longer than max_seqlen */
+  QA_DEVERR_MERGE = 4     /* decode: the split workgroups of a (sequence, kv
+                             head) did not all run on one XCD, so their partials
+                             were not merged inside the launch; that pair's
+                             rows are zeroed */
 };
 
 /*
@@ -135,9 +139,10 @@ size_t qa_workspace_bytes(int op, int batch, int n_q_heads, int n_kv_heads,
                           int max_ctx, int block_len);
 
 /*
- * Clear a workspace (its device error word) with a fill kernel on stream s.
- * Run once after allocating a workspace, before its first use.  Split-K
- * partials in the workspace are fully rewritten by every call.
+ * Clear a workspace (its device error word, and decode's merge counters) with
+ * a fill kernel on stream s.  Run once after allocating a workspace, before
+ * its first use.  Split-K partials in the workspace are fully rewritten by
+ * every call.
  */
 qa_status qa_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
@@ -178,6 +183,15 @@ qa_status qa_prefill(const qa_cache* c, const qa_params* p, const void* q,
  *   out bf16 [batch][n_q_heads][128], lse fp32 [batch][n_q_heads] or NULL
  * The launch grid depends only on (batch, heads, max_ctx), so a captured graph
  * stays valid while positions advance in device memory.
+ *   ws  workspace of qa_workspace_bytes(QA_OP_DECODE, batch, ..., max_ctx, 0)
+ *       bytes.  When batch * n_kv_heads is a multiple of 8 the split-K
+ *       partials are merged inside the one launch, through one counter per
+ *       (sequence, kv head) kept in the workspace.  The counters must be zero
+ *       when a call starts, and every call returns them to zero.  So clear
+ *       the workspace with qa_workspace_init before the first decode call, and
+ *       again after the buffer served anything else (another operation, or
+ *       decode with other batch, heads or max_ctx).  Calls sharing a
+ *       workspace must be ordered on one stream.
  */
 qa_status qa_decode(const qa_cache* c, const qa_params* p, const void* q,
                     const void* k, const void* v, const int32_t* positions,

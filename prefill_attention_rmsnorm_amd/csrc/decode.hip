@@ -10,11 +10,21 @@
 // pairs are packed as bf16x2 so P.V runs on dot2 instructions over the V rows
 // as loaded.  The four key groups of a wave are summed with lane swaps, the
 // four waves through LDS, and the workgroup writes a partial (max, sum,
-// unnormalised output) that merge.hip combines.  One more workgroup per
-// (sequence, kv head) handles the new token alone: the K prologue (fp64, one
-// RNE), the cache write, and the one-key partial of the new slot.  It reads
-// no cache rows and so runs beside the streaming workgroups instead of
-// lengthening one of them.
+// unnormalised output).  One more workgroup per (sequence, kv head) handles
+// the new token alone: the K prologue (fp64, one RNE), the cache write, and
+// the one-key partial of the new slot.  It reads no cache rows and so runs
+// beside the streaming workgroups instead of lengthening one of them.
+//
+// When the pairs fill whole rounds of the 8-XCD deal (a.sync set), the
+// partials are merged inside the launch.  Workgroups are dealt to the XCDs
+// round-robin by id, so the grid is numbered to give all of a pair's
+// workgroups one id residue mod 8, hence one XCD: their partials meet in that
+// XCD's L2.  Each workgroup stores its partial, waits for the stores and
+// counts itself in on the pair's counter with a device-scope atomic; the last
+// one checks from the counter that the pair really shared an XCD, drops its
+// L1, reads the partials from L2, merges them in split order (the same
+// arithmetic as merge.hip) and returns the counter to zero.  Otherwise
+// merge.hip runs as a second launch.
 #include <utility>
 
 #include "qa.h"
@@ -147,6 +157,105 @@ __device__ __forceinline__ void new_token(const DecodeArgs& a, const RopeFreq& f
   }
 }
 
+// Buffer loads with sc0 miss the CU's L1 and are served by the XCD's L2,
+// where the other workgroups' stores of this launch have landed.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t l2_rsrc(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes,
+                                           0x00020000);
+}
+
+// Called by every workgroup of the pair once its partial is stored.  Each
+// adds 1 + (d << 7) + (d^2 << 17) to the pair's counter, d = (XCC_ID - id)
+// mod 8: the deal may start at any XCD, but a pair's workgroups share an XCD
+// exactly when they share d, i.e. when the sums of d and d^2 are n d and
+// n d^2 for the last one's d.  A pair failing that is not merged: its rows
+// are zeroed and QA_DEVERR_MERGE is set.
+template <int G>
+__device__ __forceinline__ void merge_in_launch(const DecodeArgs& a, int pair, int b, int g) {
+  __shared__ int s_last, s_bad;
+  const int tid = threadIdx.x;
+  const unsigned ns = (unsigned)a.n_split;
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are in L2
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned d = (__builtin_amdgcn_s_getreg((3 << 11) | 20) - blockIdx.x) & 7u;
+    const unsigned add = 1u | (d << 7) | ((d * d) << 17);  // HW_REG_XCC_ID above
+    const unsigned old = __hip_atomic_fetch_add(a.sync + kSyncWords * pair, add,
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned tot = old + add;
+    s_last = (old & 0x7fu) == ns - 1u;
+    s_bad = ((tot >> 7) & 0x3ffu) != ns * d || (tot >> 17) != ns * d * d;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  asm volatile("buffer_inv sc0" ::: "memory");  // drop this CU's L1 lines
+  const bool bad = s_bad;
+  if (tid == 0) {
+    __hip_atomic_store(a.sync + kSyncWords * pair, 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    if (bad) flag_error(a.err, QA_DEVERR_MERGE);
+  }
+  if (tid >= G * 32) return;
+  const int hl = tid >> 5, d4 = (tid & 31) * 4;
+  const size_t nrow = (size_t)ns * G;
+  const __amdgpu_buffer_rsrc_t rm = l2_rsrc(a.part_m + (size_t)pair * nrow, nrow * 4);
+  const __amdgpu_buffer_rsrc_t rl = l2_rsrc(a.part_l + (size_t)pair * nrow, nrow * 4);
+  const __amdgpu_buffer_rsrc_t ro =
+      l2_rsrc(a.part_o + (size_t)pair * nrow * kHeadDim, nrow * kHeadDim * 4);
+  const float ninf = -__builtin_inff();
+  float mm = ninf, ll = 0.f;
+  float4 oo = make_float4(0.f, 0.f, 0.f, 0.f);
+  constexpr int CH = 32;
+  for (int s0 = 0; s0 < (int)ns; s0 += CH) {
+    float mv[CH], lv[CH];
+    float4 ov[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int s = s0 + c;
+      mv[c] = ninf;
+      lv[c] = 0.f;
+      ov[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (s < (int)ns) {
+        const int row = s * G + hl;
+        mv[c] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rm, row * 4, 0, 1));
+        lv[c] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, row * 4, 0, 1));
+        const auto o4 =
+            __builtin_amdgcn_raw_buffer_load_b128(ro, (row * kHeadDim + d4) * 4, 0, 1);
+        ov[c] = make_float4(__uint_as_float(o4[0]), __uint_as_float(o4[1]),
+                            __uint_as_float(o4[2]), __uint_as_float(o4[3]));
+      }
+    }
+    float mc = ninf;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) mc = fmaxf(mc, mv[c]);
+    const float mn = fmaxf(mm, mc);
+    if (mn == ninf) continue;
+    const float alpha = (mm == ninf) ? 0.f : __builtin_amdgcn_exp2f(mm - mn);
+    ll *= alpha;
+    oo.x *= alpha; oo.y *= alpha; oo.z *= alpha; oo.w *= alpha;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      if (mv[c] == ninf) continue;
+      const float wgt = __builtin_amdgcn_exp2f(mv[c] - mn);
+      ll += wgt * lv[c];
+      oo.x += wgt * ov[c].x; oo.y += wgt * ov[c].y;
+      oo.z += wgt * ov[c].z; oo.w += wgt * ov[c].w;
+    }
+    mm = mn;
+  }
+  const bool good = !bad && ll > 0.f;
+  const float inv = good ? 1.0f / ll : 0.f;
+  const size_t orow = ((size_t)b * a.n_q_heads + g * G + hl) * kHeadDim;
+  u32x2 pr = {0u, 0u};
+  if (good) {
+    pr[0] = pack_bf16x2(oo.x * inv, oo.y * inv);
+    pr[1] = pack_bf16x2(oo.z * inv, oo.w * inv);
+  }
+  *reinterpret_cast<u32x2*>(a.out + orow + d4) = pr;
+  if (a.lse && d4 == 0)
+    a.lse[(size_t)b * a.n_q_heads + g * G + hl] = good ? (mm + __log2f(ll)) * kLn2 : 0.f;
+}
+
 // NT: 16-key tiles per split.  Tiles are scored in pairs (2m, 2m+1) so the
 // weights of keys k and k+16 pack into one bf16x2; wave w scores pairs
 // w, w+4, ...  Thread (kg, c) holds V rows kg + 16i (i < NT), dims 8c..8c+7.
@@ -166,12 +275,18 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a, RopeFreq f) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   // One-dimensional grid: the cache splits of every pair first, then the
   // new-token workgroups, so the streaming workgroups are dealt out to the
-  // CUs evenly and the small ones fill in behind them.
+  // CUs evenly and the small ones fill in behind them.  With the in-launch
+  // merge, id 8 * (split * npair / 8 + k) + x is split `split` of pair
+  // x + 8k, so a pair's workgroups share id mod 8.
   const int nc = a.n_split - 1;  // cache splits
   const int npair = a.batch * a.n_kv_heads;
   const int bid = blockIdx.x;
   int pair, split;
-  if (bid < npair * nc) {
+  if (a.sync) {
+    const int ppx = npair >> 3, idx = bid >> 3;
+    split = idx / ppx;
+    pair = (bid & 7) + 8 * (idx - split * ppx);
+  } else if (bid < npair * nc) {
     pair = bid / nc;
     split = bid - pair * nc;
   } else {
@@ -186,9 +301,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a, RopeFreq f) {
   const size_t pairidx = (size_t)pair;
   const size_t rowbase = (pairidx * a.n_split + split) * G;
   const float ninf = -__builtin_inff();
+  do {  // every path ends at the merge below
   if (split == nc) {
     new_token<G>(a, f, b, g, pos, ok, rowbase, s_q, &s_red[0][0][0]);
-    return;
+    break;
   }
   // Cache rows [0, pos) -- everything before the new slot -- in nc
   // near-equal runs, so every workgroup streams the same number of rows
@@ -202,7 +318,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a, RopeFreq f) {
       a.part_m[rowbase + tid] = ninf;
       a.part_l[rowbase + tid] = 0.f;
     }
-    return;
+    break;
   }
   const uint16_t* kbase = a.c.k + (size_t)b * a.c.sb + (size_t)g * a.c.sh;
   const uint16_t* vbase = a.c.v + (size_t)b * a.c.sb + (size_t)g * a.c.sh;
@@ -359,6 +475,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a, RopeFreq f) {
       a.part_l[rowbase + hl] = (s_sum[0][hl] + s_sum[1][hl]) + (s_sum[2][hl] + s_sum[3][hl]);
     }
   }
+  } while (0);
+  if (a.sync) merge_in_launch<G>(a, pair, b, g);
 }
 
 template <int G, int NT>
@@ -383,6 +501,8 @@ using kTiles = std::make_integer_sequence<int, kDecodeMaxTiles>;
 hipError_t launch_decode(const DecodeArgs& a, const RopeFreq& f, int group,
                          hipStream_t s, int* n_kernels) {
   *n_kernels = 0;
+  if (a.sync && ((a.batch * a.n_kv_heads) % 8 != 0 || a.n_split > kInlineMaxSplits))
+    return hipErrorInvalidValue;  // the grid numbering and the counter fields
   hipError_t e;
   switch (group) {
     case 1: e = launch_decode_g<1>(a, f, s, kTiles{}); break;
@@ -393,6 +513,7 @@ hipError_t launch_decode(const DecodeArgs& a, const RopeFreq& f, int group,
   }
   if (e != hipSuccess) return e;
   *n_kernels = 1;
+  if (a.sync) return hipSuccess;  // merged inside the launch
   e = launch_merge(a, group, s);
   if (e == hipSuccess) *n_kernels = 2;
   return e;

@@ -1,4 +1,5 @@
-// Log-sum-exp merge of split-K partials (decode and verify).
+// Log-sum-exp merge of split-K partials (verify, and decode launches that do
+// not merge inside their own launch).
 //
 // Each split workgroup of decode.hip / verify.hip wrote, per query row, the
 // row's max m (log2 units), sum l and unnormalised output o over its keys.

@@ -304,6 +304,9 @@ static qa_status fill_split_args(qa::DecodeArgs& a, const qa_cache* c,
   a.part_m = reinterpret_cast<float*>(base + L.m_off);
   a.part_l = reinterpret_cast<float*>(base + L.l_off);
   a.part_o = reinterpret_cast<float*>(base + L.o_off);
+  a.sync = L.sync_off && qa::decode_merges_inline(batch, c->n_kv_heads, L.n_split)
+               ? reinterpret_cast<unsigned*>(base + L.sync_off)
+               : nullptr;
   return QA_OK;
 }
 

@@ -31,6 +31,7 @@ struct SplitLayout {
   int keys_per_split;
   int n_split;
   size_t m_off, l_off, o_off, total;
+  size_t sync_off = 0;  // decode only: the in-launch merge counters
 };
 
 // Decode: keys per split-K block, a multiple of 16 (one score tile) of at
@@ -72,11 +73,26 @@ inline SplitLayout split_layout(int batch, int n_kv, int rows, int max_ctx,
 }
 
 // Decode partials: the cache splits (rows before the new slot) and one for
-// the new token.
+// the new token.  Then one 128-byte line per (sequence, kv head) holding the
+// arrival counter of the in-launch merge: zero after qa_workspace_init, and
+// returned to zero by every call.
+constexpr size_t kSyncLine = 128;
+constexpr int kSyncWords = (int)(kSyncLine / 4);
 inline SplitLayout decode_split_layout(int batch, int n_kv, int G, int max_ctx) {
   const int rows_before = max_ctx > 1 ? max_ctx - 1 : 1;
-  return split_layout(batch, n_kv, G, rows_before,
-                      decode_keys_per_split(batch, n_kv, rows_before), 1);
+  SplitLayout L = split_layout(batch, n_kv, G, rows_before,
+                               decode_keys_per_split(batch, n_kv, rows_before), 1);
+  L.sync_off = L.total;
+  L.total = L.sync_off + round256((size_t)batch * n_kv * kSyncLine);
+  return L;
+}
+
+// The in-launch merge needs the pairs to fill whole rounds of the 8-XCD deal
+// and at most 127 splits (the counter's fields); other launches merge in a
+// second kernel.
+constexpr int kInlineMaxSplits = 127;
+inline bool decode_merges_inline(int batch, int n_kv, int n_split) {
+  return ((long)batch * n_kv) % 8 == 0 && n_split <= kInlineMaxSplits;
 }
 
 // Prefill: the header, then the cos/sin table float2 [total_tokens][64] that
@@ -137,6 +153,7 @@ struct DecodeArgs {
   float* part_m;
   float* part_l;
   float* part_o;
+  unsigned* sync;  // decode: merge counters (kSyncWords apart); NULL: merge kernel
 };
 
 // ---- launchers (return the hipError_t of the launch) ------------------------------

@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libqa.so")
 
 QA_OP_PREFILL, QA_OP_DECODE, QA_OP_VERIFY = 0, 1, 2
-QA_DEVERR_POSITION, QA_DEVERR_SEQLENS = 1, 2
+QA_DEVERR_POSITION, QA_DEVERR_SEQLENS, QA_DEVERR_MERGE = 1, 2, 4
 HEAD_DIM = 128
 
 EXPORTS = (

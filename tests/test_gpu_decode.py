@@ -177,6 +177,39 @@ def test_invalid_position_flags_and_zeroes():
     assert torch.isfinite(out[0].float()).all()
 
 
+@pytest.mark.parametrize("B,lens", [(4, [250, 120, 7, 299]), (3, [250, 120, 7])])
+def test_merge_counters_left_at_zero(B, lens):
+    # With B x Hkv a multiple of 8 (here 8 pairs) the split-K partials are
+    # merged inside the decode launch, by the last workgroup of each (sequence,
+    # kv head) to count in on a counter in the workspace; otherwise (6 pairs)
+    # a second kernel merges them.  Either way every call must leave the
+    # counters at zero (as a fresh workspace has them), flag nothing, and give
+    # the same bytes call after call and as a fresh workspace does.
+    Hq, Hkv, cap = 8, 2, 300
+    cache, _ = _seeded_prefix(B, Hkv, cap, lens, 31)
+    q = W.normal_bf16((B, Hq, 128), 31, 1, 0, "q").cuda()
+    k = W.normal_bf16((B, Hkv, 128), 31, 1, 0, "k").cuda()
+    v = W.normal_bf16((B, Hkv, 128), 31, 1, 0, "v").cuda()
+    pos = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    p = params(Hq)
+    ws = qa.workspace(qa.QA_OP_DECODE, B, Hq, Hkv, cap)
+    fresh = ws.clone()
+    outs = []
+    for _ in range(5):
+        out, _, _ = qa.decode(cache, p, q, k, v, pos, cap, ws=ws)
+        outs.append(out.clone())
+    torch.cuda.synchronize()
+    assert qa.device_error(ws) == 0
+    n, tail = ws.numel(), 256 * ((B * Hkv * 128 + 255) // 256)  # counters close the layout
+    assert torch.equal(ws[n - tail:], fresh[n - tail:])
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    ref, _, ws2 = qa.decode(cache, p, q, k, v, pos, cap)
+    assert qa.device_error(ws2) == 0
+    assert torch.equal(ref.view(torch.int16), outs[0].view(torch.int16))
+    say(f"  B={B}: {B * Hkv} pairs, 5 calls on one workspace, counters back at zero")
+
+
 def test_deterministic_rerun():
     B, Hq, Hkv, cap = 4, 32, 8, 1100
     cache, _ = _seeded_prefix(B, Hkv, cap, [1000, 900, 1099, 3], 29)
