@@ -421,6 +421,11 @@ def main():
             f"verify {v * 1e3:.1f} us")
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    # every workspace's device error word after the timed steps (a position
+    # out of range, bad sequence offsets, or an in-launch merge that could not
+    # prove its placement): nonzero means the timed outputs are not valid
+    dev_err = {"prefill": qa.device_error(wl.pws), "decode": qa.device_error(wl.dws),
+               "verify": qa.device_error(wl.vws)}
     K = args.steps
     ms_per_step = sum(per_step) / K
     pre_ms = phase["prefill"] / K
@@ -500,6 +505,7 @@ def main():
                              "frac": round(pre_ach / MFMA_BF16_PEAK_TFLOPS, 4),
                              "flops_per_launch": pflops,
                              "avg_launch_us": round(pre_call_us, 2)},
+        "device_errors": dev_err,
         "wall_s_timed": round(wall, 3),
         "provenance": build_info(),
     }
@@ -512,6 +518,9 @@ def main():
         log("bench: cpu baseline (fp64 oracle, bounded sample)")
         result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result), flush=True)
+    if any(dev_err.values()):
+        log(f"bench: device error words are not zero: {dev_err}")
+        sys.exit(3)
 
 
 if __name__ == "__main__":

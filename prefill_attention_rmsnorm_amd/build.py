@@ -25,7 +25,7 @@ ARCH = "gfx950"
 SOURCES = ["qa_api.cpp", "util.hip", "prefill.hip", "decode.hip", "verify.hip",
            "merge.hip", "rmsnorm.hip"]
 HEADERS = ["qa_internal.h", "qa_device.h", "attn_tile.h", "rmsnorm.h",
-           "verify_layout.h"]
+           "verify_layout.h", "merge_count.h"]
 
 
 def hipcc() -> str:
@@ -82,7 +82,7 @@ def _write_build_info():
         "hipcc": ver[0] if ver else "",
         "arch": ARCH,
         "decode_source_sha": _sha(["decode.hip", "merge.hip", "qa_device.h",
-                                   "qa_internal.h"]),
+                                   "qa_internal.h", "merge_count.h"]),
         "prefill_source_sha": _sha(["prefill.hip", "attn_tile.h",
                                     "qa_device.h", "qa_internal.h"]),
         "verify_source_sha": _sha(["verify.hip", "attn_tile.h", "qa_device.h",

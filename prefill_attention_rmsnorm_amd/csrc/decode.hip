@@ -165,34 +165,36 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t l2_rsrc(const void* base, size
 }
 
 // Called by every workgroup of the pair once its partial is stored.  Each
-// adds 1 + (d << 7) + (d^2 << 17) to the pair's counter, d = (XCC_ID - id)
-// mod 8: the deal may start at any XCD, but a pair's workgroups share an XCD
-// exactly when they share d, i.e. when the sums of d and d^2 are n d and
-// n d^2 for the last one's d.  A pair failing that is not merged: its rows
-// are zeroed and QA_DEVERR_MERGE is set.
+// adds merge_count_add(d) to the pair's counter, d = (XCC_ID - id) mod 8:
+// the deal may start at any XCD, but a pair's workgroups share an XCD
+// exactly when they share d (merge_count.h).  A pair failing that is not
+// merged: its rows are zeroed and QA_DEVERR_MERGE is set.  An arriver that
+// finds a counter value no zeroed counter can reach (memory the counter
+// shares with other use, not cleared by qa_workspace_init) sets
+// QA_DEVERR_MERGE too; that pair's rows are then undefined.
 template <int G>
 __device__ __forceinline__ void merge_in_launch(const DecodeArgs& a, int pair, int b, int g) {
   __shared__ int s_last, s_bad;
   const int tid = threadIdx.x;
   const unsigned ns = (unsigned)a.n_split;
+  unsigned* ctr = a.sync - kSyncWords * (pair + 1);
   __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are in L2
   __syncthreads();
   if (tid == 0) {
     const unsigned d = (__builtin_amdgcn_s_getreg((3 << 11) | 20) - blockIdx.x) & 7u;
-    const unsigned add = 1u | (d << 7) | ((d * d) << 17);  // HW_REG_XCC_ID above
-    const unsigned old = __hip_atomic_fetch_add(a.sync + kSyncWords * pair, add,
-                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned tot = old + add;
-    s_last = (old & 0x7fu) == ns - 1u;
-    s_bad = ((tot >> 7) & 0x3ffu) != ns * d || (tot >> 17) != ns * d * d;
+    const unsigned add = merge_count_add(d);  // HW_REG_XCC_ID above
+    const unsigned old =
+        __hip_atomic_fetch_add(ctr, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!merge_count_valid(old, ns)) flag_error(a.err, QA_DEVERR_MERGE);
+    s_last = merge_count_last(old, ns);
+    s_bad = !merge_count_one_xcd(old + add, ns, d);
   }
   __syncthreads();
   if (!s_last) return;
   asm volatile("buffer_inv sc0" ::: "memory");  // drop this CU's L1 lines
   const bool bad = s_bad;
   if (tid == 0) {
-    __hip_atomic_store(a.sync + kSyncWords * pair, 0u, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (bad) flag_error(a.err, QA_DEVERR_MERGE);
   }
   if (tid >= G * 32) return;
@@ -202,58 +204,16 @@ __device__ __forceinline__ void merge_in_launch(const DecodeArgs& a, int pair, i
   const __amdgpu_buffer_rsrc_t rl = l2_rsrc(a.part_l + (size_t)pair * nrow, nrow * 4);
   const __amdgpu_buffer_rsrc_t ro =
       l2_rsrc(a.part_o + (size_t)pair * nrow * kHeadDim, nrow * kHeadDim * 4);
-  const float ninf = -__builtin_inff();
-  float mm = ninf, ll = 0.f;
-  float4 oo = make_float4(0.f, 0.f, 0.f, 0.f);
-  constexpr int CH = 32;
-  for (int s0 = 0; s0 < (int)ns; s0 += CH) {
-    float mv[CH], lv[CH];
-    float4 ov[CH];
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int s = s0 + c;
-      mv[c] = ninf;
-      lv[c] = 0.f;
-      ov[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (s < (int)ns) {
-        const int row = s * G + hl;
-        mv[c] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rm, row * 4, 0, 1));
-        lv[c] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, row * 4, 0, 1));
-        const auto o4 =
-            __builtin_amdgcn_raw_buffer_load_b128(ro, (row * kHeadDim + d4) * 4, 0, 1);
-        ov[c] = make_float4(__uint_as_float(o4[0]), __uint_as_float(o4[1]),
-                            __uint_as_float(o4[2]), __uint_as_float(o4[3]));
-      }
-    }
-    float mc = ninf;
-#pragma unroll
-    for (int c = 0; c < CH; ++c) mc = fmaxf(mc, mv[c]);
-    const float mn = fmaxf(mm, mc);
-    if (mn == ninf) continue;
-    const float alpha = (mm == ninf) ? 0.f : __builtin_amdgcn_exp2f(mm - mn);
-    ll *= alpha;
-    oo.x *= alpha; oo.y *= alpha; oo.z *= alpha; oo.w *= alpha;
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      if (mv[c] == ninf) continue;
-      const float wgt = __builtin_amdgcn_exp2f(mv[c] - mn);
-      ll += wgt * lv[c];
-      oo.x += wgt * ov[c].x; oo.y += wgt * ov[c].y;
-      oo.z += wgt * ov[c].z; oo.w += wgt * ov[c].w;
-    }
-    mm = mn;
-  }
-  const bool good = !bad && ll > 0.f;
-  const float inv = good ? 1.0f / ll : 0.f;
-  const size_t orow = ((size_t)b * a.n_q_heads + g * G + hl) * kHeadDim;
-  u32x2 pr = {0u, 0u};
-  if (good) {
-    pr[0] = pack_bf16x2(oo.x * inv, oo.y * inv);
-    pr[1] = pack_bf16x2(oo.z * inv, oo.w * inv);
-  }
-  *reinterpret_cast<u32x2*>(a.out + orow + d4) = pr;
-  if (a.lse && d4 == 0)
-    a.lse[(size_t)b * a.n_q_heads + g * G + hl] = good ? (mm + __log2f(ll)) * kLn2 : 0.f;
+  const MergeOut mo = merge_splits<32>((int)ns, [&](int s, float& m, float& l, float4& o) {
+    const int row = s * G + hl;
+    m = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rm, row * 4, 0, 1));
+    l = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, row * 4, 0, 1));
+    const auto o4 = __builtin_amdgcn_raw_buffer_load_b128(ro, (row * kHeadDim + d4) * 4, 0, 1);
+    o = make_float4(__uint_as_float(o4[0]), __uint_as_float(o4[1]), __uint_as_float(o4[2]),
+                    __uint_as_float(o4[3]));
+  });
+  const size_t hrow = (size_t)b * a.n_q_heads + g * G + hl;
+  store_merged(mo, bad, a.out + hrow * kHeadDim + d4, a.lse && d4 == 0 ? a.lse + hrow : nullptr);
 }
 
 // NT: 16-key tiles per split.  Tiles are scored in pairs (2m, 2m+1) so the

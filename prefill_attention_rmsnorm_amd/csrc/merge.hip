@@ -23,22 +23,20 @@ __global__ __launch_bounds__(128) void merge_kernel(DecodeArgs a, int G) {
   const int b = pair / a.n_kv_heads, g = pair % a.n_kv_heads;
   const int rr = item >> 5, d4 = (item & 31) * 4;
   const size_t r0 = (size_t)pair * a.n_split * rows + rr;
-  const MergeOut mo = merge_splits<32>(a.part_m + r0, a.part_l + r0,
-                                   a.part_o + r0 * kHeadDim + d4, a.n_split, rows);
-  const bool good = mo.l > 0.f;
-  const float inv = good ? 1.0f / mo.l : 0.f;
+  const float* pm = a.part_m + r0;
+  const float* pl = a.part_l + r0;
+  const float* po = a.part_o + r0 * kHeadDim + d4;
+  const MergeOut mo = merge_splits<32>(a.n_split, [&](int s, float& m, float& l, float4& o) {
+    m = pm[(size_t)s * rows];
+    l = pl[(size_t)s * rows];
+    o = *reinterpret_cast<const float4*>(po + (size_t)s * rows * kHeadDim);
+  });
   const int n = a.block_len;
   const int hl = rr / n, ti = rr % n;
   const size_t orow = (((size_t)b * n + ti) * a.n_q_heads + g * G + hl) * kHeadDim;
-  u32x2 pr = {0u, 0u};
-  if (good) {
-    pr[0] = pack_bf16x2(mo.o.x * inv, mo.o.y * inv);
-    pr[1] = pack_bf16x2(mo.o.z * inv, mo.o.w * inv);
-  }
-  *reinterpret_cast<u32x2*>(a.out + orow + d4) = pr;
-  if (a.lse && d4 == 0)
-    a.lse[((size_t)b * n + ti) * a.n_q_heads + g * G + hl] =
-        good ? (mo.m + __log2f(mo.l)) * kLn2 : 0.f;
+  store_merged(mo, false, a.out + orow + d4,
+               a.lse && d4 == 0 ? a.lse + ((size_t)b * n + ti) * a.n_q_heads + g * G + hl
+                                : nullptr);
 }
 
 hipError_t launch_merge(const DecodeArgs& a, int group, hipStream_t s) {

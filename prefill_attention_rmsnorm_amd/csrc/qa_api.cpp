@@ -280,7 +280,7 @@ static qa_status fill_split_args(qa::DecodeArgs& a, const qa_cache* c,
                                  const void* k, const void* v,
                                  const int32_t* pos, int batch, int block_len,
                                  int max_ctx, void* out, float* lse, void* ws,
-                                 const qa::SplitLayout& L) {
+                                 size_t ws_bytes, const qa::SplitLayout& L) {
   a.c = cache_args(c);
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -305,7 +305,7 @@ static qa_status fill_split_args(qa::DecodeArgs& a, const qa_cache* c,
   a.part_l = reinterpret_cast<float*>(base + L.l_off);
   a.part_o = reinterpret_cast<float*>(base + L.o_off);
   a.sync = L.sync_off && qa::decode_merges_inline(batch, c->n_kv_heads, L.n_split)
-               ? reinterpret_cast<unsigned*>(base + L.sync_off)
+               ? reinterpret_cast<unsigned*>(base + qa::decode_sync_end(ws_bytes))
                : nullptr;
   return QA_OK;
 }
@@ -333,7 +333,7 @@ qa_status qa_decode(const qa_cache* c, const qa_params* p, const void* q,
   QA_REQUIRE(ws_bytes >= L.total, QA_ERR_WORKSPACE,
              "workspace %zu bytes < %zu needed", ws_bytes, L.total);
   qa::DecodeArgs a;
-  fill_split_args(a, c, p, q, k, v, positions, batch, 1, max_ctx, out, lse, ws, L);
+  fill_split_args(a, c, p, q, k, v, positions, batch, 1, max_ctx, out, lse, ws, ws_bytes, L);
   int nk = 0;
   hipError_t e = qa::launch_decode(a, make_freq(p->rope_theta), G,
                                    static_cast<hipStream_t>(stream), &nk);
@@ -371,7 +371,7 @@ qa_status qa_verify(const qa_cache* c, const qa_params* p, const void* q,
              "workspace %zu bytes < %zu needed", ws_bytes, L.total);
   qa::DecodeArgs a;
   fill_split_args(a, c, p, q, k, v, start_pos, batch, block_len, max_ctx, out, lse,
-                  ws, L);
+                  ws, ws_bytes, L);
   int nk = 0;
   hipError_t e = qa::launch_verify(a, make_freq(p->rope_theta), G,
                                    static_cast<hipStream_t>(stream), &nk);

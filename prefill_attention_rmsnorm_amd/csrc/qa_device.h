@@ -129,17 +129,17 @@ __device__ __forceinline__ void sincos_reduced(double a, float* s, float* c) {
 }
 
 // Log-sum-exp merge of n_split partial rows (m: max in log2 units, l: sum,
-// o: unnormalised output) for 4 consecutive dims of one row.  Loads are
-// issued CH splits at a time so that a merge costs one memory round trip per
-// CH splits.  stride_row: floats between consecutive splits of m/l (= rows).
+// o: unnormalised output) for 4 consecutive dims of one row, in split order.
+// load(s, m, l, o) fetches split s's values; loads are issued CH splits at a
+// time so that a merge costs one memory round trip per CH splits.  Both
+// merge paths (the merge kernel and decode's in-launch merge) run this one
+// piece of arithmetic and differ only in how they load.
 struct MergeOut {
   float m, l;
   float4 o;
 };
-template <int CH = 16>
-__device__ __forceinline__ MergeOut merge_splits(const float* pm, const float* pl,
-                                                 const float* po, int n_split,
-                                                 int rows) {
+template <int CH, class Load>
+__device__ __forceinline__ MergeOut merge_splits(int n_split, Load&& load) {
   const float ninf = -__builtin_inff();
   MergeOut r;
   r.m = ninf;
@@ -154,11 +154,7 @@ __device__ __forceinline__ MergeOut merge_splits(const float* pm, const float* p
       mv[c] = ninf;
       lv[c] = 0.f;
       ov[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (s < n_split) {
-        mv[c] = pm[(size_t)s * rows];
-        lv[c] = pl[(size_t)s * rows];
-        ov[c] = *reinterpret_cast<const float4*>(po + (size_t)s * rows * kHeadDim);
-      }
+      if (s < n_split) load(s, mv[c], lv[c], ov[c]);
     }
     float mc = ninf;
 #pragma unroll
@@ -179,6 +175,21 @@ __device__ __forceinline__ MergeOut merge_splits(const float* pm, const float* p
     r.m = mn;
   }
   return r;
+}
+
+// The merged row as bf16 output (4 dims) and natural-log LSE; a row with no
+// visible key (l = 0), or one the caller marks bad, becomes zeros.
+__device__ __forceinline__ void store_merged(const MergeOut& mo, bool bad, uint16_t* orow4,
+                                             float* lse) {
+  const bool good = !bad && mo.l > 0.f;
+  const float inv = good ? 1.0f / mo.l : 0.f;
+  u32x2 pr = {0u, 0u};
+  if (good) {
+    pr[0] = pack_bf16x2(mo.o.x * inv, mo.o.y * inv);
+    pr[1] = pack_bf16x2(mo.o.z * inv, mo.o.w * inv);
+  }
+  *reinterpret_cast<u32x2*>(orow4) = pr;
+  if (lse) *lse = good ? (mo.m + __log2f(mo.l)) * kLn2 : 0.f;
 }
 
 __device__ __forceinline__ void flag_error(int* err, int bits) {

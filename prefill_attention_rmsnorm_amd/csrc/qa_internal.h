@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "merge_count.h"
+
 namespace qa {
 
 constexpr int kHeadDim = 128;
@@ -73,9 +75,12 @@ inline SplitLayout split_layout(int batch, int n_kv, int rows, int max_ctx,
 }
 
 // Decode partials: the cache splits (rows before the new slot) and one for
-// the new token.  Then one 128-byte line per (sequence, kv head) holding the
-// arrival counter of the in-launch merge: zero after qa_workspace_init, and
-// returned to zero by every call.
+// the new token.  Then room for one 128-byte line per (sequence, kv head)
+// holding the arrival counter of the in-launch merge.  The counters are
+// placed from the END of the caller's workspace downwards (pair p at
+// end - 128 (p + 1), end = ws_bytes rounded down to 128), so a workspace
+// reused for a smaller batch or context finds the same, zeroed, counters.
+// They are zero after qa_workspace_init and returned to zero by every call.
 constexpr size_t kSyncLine = 128;
 constexpr int kSyncWords = (int)(kSyncLine / 4);
 inline SplitLayout decode_split_layout(int batch, int n_kv, int G, int max_ctx) {
@@ -86,11 +91,12 @@ inline SplitLayout decode_split_layout(int batch, int n_kv, int G, int max_ctx) 
   L.total = L.sync_off + round256((size_t)batch * n_kv * kSyncLine);
   return L;
 }
+// End of the counter block for a workspace of ws_bytes (bytes from its start).
+inline size_t decode_sync_end(size_t ws_bytes) { return ws_bytes & ~(kSyncLine - 1); }
 
 // The in-launch merge needs the pairs to fill whole rounds of the 8-XCD deal
 // and at most 127 splits (the counter's fields); other launches merge in a
 // second kernel.
-constexpr int kInlineMaxSplits = 127;
 inline bool decode_merges_inline(int batch, int n_kv, int n_split) {
   return ((long)batch * n_kv) % 8 == 0 && n_split <= kInlineMaxSplits;
 }
@@ -153,7 +159,8 @@ struct DecodeArgs {
   float* part_m;
   float* part_l;
   float* part_o;
-  unsigned* sync;  // decode: merge counters (kSyncWords apart); NULL: merge kernel
+  unsigned* sync;  // decode: END of the merge counters (pair p's at sync - kSyncWords (p+1));
+                   // NULL: merge kernel
 };
 
 // ---- launchers (return the hipError_t of the launch) ------------------------------

@@ -131,20 +131,32 @@ def _need(t, name, dtype, numel=None):
 
 
 class Cache:
-    """A qa_cache over caller-owned bf16 tensors k, v [B, Hkv, cap, 128]."""
+    """A qa_cache over caller-owned bf16 tensors k, v [B, Hkv, cap, 128].
+
+    k and v may be strided views (a padded slot pitch, a token-major or a
+    slot-major buffer viewed as [B, Hkv, cap, 128]) as long as the head_dim
+    axis is dense, both share one set of strides, and every stride is a
+    multiple of 8 elements; the descriptor carries the strides and the
+    library validates them at every call.
+    """
 
     def __init__(self, k: torch.Tensor, v: torch.Tensor):
         if k.shape != v.shape or k.dim() != 4 or k.shape[3] != HEAD_DIM:
             raise ValueError("k, v must be [batch, n_kv_heads, capacity, 128]")
         _need(k, "cache k", torch.bfloat16)
         _need(v, "cache v", torch.bfloat16)
-        if not (k.is_contiguous() and v.is_contiguous()):
-            raise ValueError("cache tensors must be contiguous")
+        if k.stride() != v.stride() or k.stride(3) != 1:
+            raise ValueError("cache k and v must share strides with a dense "
+                             "head_dim axis")
         self.k, self.v = k, v
-        self.desc = QaCache()
         B, H, cap, d = k.shape
-        _check(lib().qa_cache_alloc(ctypes.byref(self.desc), B, H, cap, d,
-                                    _ptr(k), _ptr(v)))
+        self.desc = QaCache()
+        if k.is_contiguous():
+            _check(lib().qa_cache_alloc(ctypes.byref(self.desc), B, H, cap, d,
+                                        _ptr(k), _ptr(v)))
+        else:
+            sb, sh, sp, _ = k.stride()
+            self.desc = QaCache(_ptr(k), _ptr(v), B, H, cap, d, sb, sh, sp, 0)
 
     @staticmethod
     def empty(batch, n_kv_heads, capacity, device="cuda", fill_bits=0x7FC1):

@@ -222,3 +222,46 @@ def test_deterministic_rerun():
     a = a.clone()
     b, _, _ = qa.decode(cache, params(Hq), q, k, v, pos, cap, ws=ws)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_stale_merge_counters_are_flagged():
+    # A decode workspace that served a prefill (its cos/sin table written over
+    # the merge counters) and was not cleared again: the in-launch merge must
+    # not run silently on those counters -- the call sets QA_DEVERR_MERGE.
+    # After qa_workspace_init the same buffer gives the fresh-workspace result.
+    B, Hq, Hkv, cap = 4, 8, 2, 300
+    lens = [250, 120, 7, 299]
+    cache, _ = _seeded_prefix(B, Hkv, cap, lens, 32)
+    q = W.normal_bf16((B, Hq, 128), 32, 1, 0, "q").cuda()
+    k = W.normal_bf16((B, Hkv, 128), 32, 1, 0, "k").cuda()
+    v = W.normal_bf16((B, Hkv, 128), 32, 1, 0, "v").cuda()
+    pos = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    p = params(Hq)
+    ws = qa.workspace(qa.QA_OP_DECODE, B, Hq, Hkv, cap)
+    n = ws.numel()
+    # the largest prefill whose table fits: it covers all but the last
+    # 256 bytes of the buffer, i.e. the counters of pairs 2 .. 7
+    T = (n - 256) // 512
+    assert 256 + T * 512 >= n - 256 and qa.workspace_bytes(
+        qa.QA_OP_PREFILL, 1, Hq, Hkv, T) <= n
+    pc = new_cache(1, Hkv, T)
+    pq = W.normal_bf16((T, Hq, 128), 32, 2, 0, "q").cuda()
+    pk = W.normal_bf16((T, Hkv, 128), 32, 2, 0, "k").cuda()
+    pv = W.normal_bf16((T, Hkv, 128), 32, 2, 0, "v").cuda()
+    cu, ppos = W.packed_layout([T])
+    qa.prefill(pc, p, pq, pk, pv, torch.from_numpy(cu).cuda(),
+               torch.from_numpy(ppos).cuda(), T, ws=ws)
+    assert qa.device_error(ws) == 0
+    qa.decode(cache, p, q, k, v, pos, cap, ws=ws)
+    code = qa.device_error(ws)
+    say(f"  decode on a stale workspace: error word {code}")
+    assert code & qa.QA_DEVERR_MERGE
+    # cleared again, the buffer behaves as a fresh workspace
+    qa.lib().qa_workspace_init(qa._ptr(ws), n, qa._stream(None))
+    c2, _ = _seeded_prefix(B, Hkv, cap, lens, 32)
+    out, _, _ = qa.decode(c2, p, q, k, v, pos, cap, ws=ws)
+    out = out.clone()
+    assert qa.device_error(ws) == 0
+    c3, _ = _seeded_prefix(B, Hkv, cap, lens, 32)
+    ref, _, _ = qa.decode(c3, p, q, k, v, pos, cap)
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))

@@ -132,3 +132,83 @@ def test_rmsnorm_graph():
         out.zero_()
         res.zero_()
     _replay_check("rmsnorm_hidden", run, [out, res], disturb)
+
+
+def test_captured_multilayer_decode_step_vs_oracle():
+    """The benchmark's decode step, checked against the oracle: the qa_decode
+    calls of several layers and the on-device position increment captured in
+    one graph (one workspace shared by the layers, as in bench.py), replayed
+    step after step from position 2048 at the B=4 Qwen3-4B shape.  Fresh
+    inputs are copied into the graph's static buffers between replays; every
+    layer's output and LSE at every step is compared with oracle.decode and
+    the caches byte for byte at the end."""
+    import oracle
+
+    from .gpu_helpers import EPS, THETA, check_cache, compare, f64, prefix_fill
+
+    w = W.get(2)
+    B, Hq, Hkv, cap, S = w.batch, w.n_q_heads, w.n_kv_heads, w.capacity, 2048
+    L, NSTEP, seed = 3, 8, 90
+    say(f"captured decode step: {L} layers, {NSTEP} steps from {S}, B={B}")
+    caches, ocs = [], []
+    for l in range(L):
+        c = new_cache(B, Hkv, cap)
+        oc = oracle.Cache.empty(B, Hkv, cap, 128)
+        prefix_fill(c, oc, [S] * B, seed + l)
+        caches.append(c)
+        ocs.append(oc)
+    p = params(Hq)
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    qs = [torch.zeros((B, Hq, 128), **bf) for _ in range(L)]
+    ks = [torch.zeros((B, Hkv, 128), **bf) for _ in range(L)]
+    vs = [torch.zeros((B, Hkv, 128), **bf) for _ in range(L)]
+    outs = [torch.empty((B, Hq, 128), **bf) for _ in range(L)]
+    lses = [torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+            for _ in range(L)]
+    dpos = torch.full((B,), S, dtype=torch.int32, device="cuda")
+    ws = qa.workspace(qa.QA_OP_DECODE, B, Hq, Hkv, cap)
+
+    def step():
+        for l in range(L):
+            qa.decode(caches[l], p, qs[l], ks[l], vs[l], dpos, cap, out=outs[l],
+                      lse=lses[l], ws=ws)
+        dpos.add_(1)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm the path outside the capture
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    dpos.fill_(S)  # the warm-up's slot S is rewritten by the first replay
+    torch.cuda.synchronize()
+    pos = np.full(B, S, dtype=np.int64)
+    for st in range(NSTEP):
+        inp = []
+        for l in range(L):
+            q = W.normal_bf16((B, Hq, 128), seed, l, st, "q")
+            k = W.normal_bf16((B, Hkv, 128), seed, l, st, "k")
+            v = W.normal_bf16((B, Hkv, 128), seed, l, st, "v")
+            qs[l].copy_(q)
+            ks[l].copy_(k)
+            vs[l].copy_(v)
+            inp.append((q, k, v))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for l, (q, k, v) in enumerate(inp):
+            ref, ref_lse, ocs[l] = oracle.decode(
+                ocs[l], q.double().numpy(), k.double().numpy(),
+                v.double().numpy(), pos, scale=w.scale, theta=THETA, eps=EPS)
+            compare(f64(outs[l]), ref, f"step {st} layer {l}")
+            compare(f64(lses[l])[..., None], ref_lse[..., None],
+                    f"step {st} layer {l} lse", atol=1e-2, rrel=float("inf"),
+                    out_bf16=False)
+        pos = pos + 1
+    assert dpos.cpu().tolist() == [S + NSTEP] * B
+    assert qa.device_error(ws) == 0
+    for l in range(L):
+        check_cache(caches[l], ocs[l], f"layer {l} cache")

@@ -176,25 +176,59 @@ def test_launch_counters_prove_hip_path():
     assert after[3] >= before[3] + 2       # prologue + attention kernels
 
 
-def test_full_size_b4_s2048_sampled():
+def test_full_size_b4_s2048():
+    # one Qwen3-4B layer at B=4 x 2048: every (token, head) row and its LSE
+    # against the oracle; 1024 q-tiles over the persistent grid, so every CU
+    # takes several tiles from the counter
     w = W.get(2)
-    lens = list(w.prompt_lens)
-    T = sum(lens)
-    g = np.random.default_rng(11)
-    rows = [(int(t), int(h)) for t, h in zip(g.integers(0, T, 48),
-                                              g.integers(0, w.n_q_heads, 48))]
-    rows += [(2047, 0), (2048, 31), (T - 1, 17), (0, 5)]
-    run_prefill(lens, w.n_q_heads, w.n_kv_heads, w.capacity, seed=12, rows=rows)
+    _, _, st = run_prefill(list(w.prompt_lens), w.n_q_heads, w.n_kv_heads,
+                           w.capacity, seed=12)
+    say(f"FULLSIZE_STATS prefill_b4_s2048 {st}")
 
 
-def test_full_size_ragged_sampled():
+def test_full_size_ragged():
     w = W.get(3)
     lens = W.ragged_lengths(3, w.batch, w.ragged_choices)
-    T = sum(lens)
-    g = np.random.default_rng(13)
-    rows = [(int(t), int(h)) for t, h in zip(g.integers(0, T, 48),
-                                              g.integers(0, w.n_q_heads, 48))]
-    cu = np.cumsum([0] + lens)
-    rows += [(int(c) - 1, 3) for c in cu[1:]] + [(int(c), 9) for c in cu[:-1]]
-    run_prefill(lens, w.n_q_heads, w.n_kv_heads, w.capacity, seed=14,
-                rows=rows)
+    _, _, st = run_prefill(lens, w.n_q_heads, w.n_kv_heads, w.capacity,
+                           seed=14)
+    say(f"FULLSIZE_STATS prefill_ragged {lens} {st}")
+
+
+def test_chunked_prefill_full_size():
+    # B=4 prompts of 2048 fed as four 512-token chunks per sequence, each
+    # chunk attending to the slots the earlier chunks wrote; every row of
+    # every chunk and the final cache against the oracle
+    w = W.get(2)
+    B, Hq, Hkv, cap, S, C = (w.batch, w.n_q_heads, w.n_kv_heads, w.capacity,
+                             w.prompt_lens[0], 512)
+    seed = 15
+    say(f"chunked prefill: B={B} S={S} chunk={C}")
+    q = W.normal_bf16((B, S, Hq, 128), seed, 0, 0, "q")
+    k = W.normal_bf16((B, S, Hkv, 128), seed, 0, 0, "k")
+    v = W.normal_bf16((B, S, Hkv, 128), seed, 0, 0, "v")
+    cache = new_cache(B, Hkv, cap)
+    oc = oracle.Cache.empty(B, Hkv, cap, 128)
+    p = params(Hq)
+    ws = qa.workspace(qa.QA_OP_PREFILL, B, Hq, Hkv, B * C)
+    lse = torch.empty((B * C, Hq), device="cuda")
+    seq = seq_index([C] * B)
+    stats = []
+    for c0 in range(0, S, C):
+        qc = q[:, c0:c0 + C].reshape(B * C, Hq, 128)
+        kc = k[:, c0:c0 + C].reshape(B * C, Hkv, 128)
+        vc = v[:, c0:c0 + C].reshape(B * C, Hkv, 128)
+        cu, pos = W.packed_layout([C] * B, [c0] * B)
+        out, _, _ = qa.prefill(cache, p, qc.cuda(), kc.cuda(), vc.cuda(),
+                               torch.from_numpy(cu).cuda(),
+                               torch.from_numpy(pos).cuda(), C, lse=lse, ws=ws)
+        oc = oracle.write_kv(oc, kc.double().numpy(), vc.double().numpy(), seq,
+                             pos, theta=THETA, eps=EPS)
+        ref, ref_lse = oracle.attend_tokens(oc, qc.double().numpy(), seq, pos,
+                                            scale=1 / np.sqrt(128), theta=THETA,
+                                            eps=EPS)
+        stats.append(compare(f64(out), ref, f"chunk at {c0}"))
+        compare(f64(lse)[..., None], ref_lse[..., None], f"chunk lse at {c0}",
+                atol=1e-2, rrel=float("inf"), out_bf16=False)
+    assert qa.device_error(ws) == 0
+    check_cache(cache, oc)
+    say(f"FULLSIZE_STATS prefill_chunked_4x512 {stats[-1]}")
