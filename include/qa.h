@@ -199,6 +199,27 @@ qa_status qa_decode(const qa_cache* c, const qa_params* p, const void* q,
                     size_t ws_bytes, void* stream);
 
 /*
+ * qa_decode without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, kernels and results as qa_decode, except
+ * that the split-K partials and the in-launch merge counters live in a
+ * library-held device array of 16 MiB per GPU (held until the process ends),
+ * and device-side errors (QA_DEVERR_* bits) are OR-ed into *dev_err, a
+ * caller-owned device int32 (NULL: not reported).  Sizes whose decode
+ * workspace (qa_workspace_bytes(QA_OP_DECODE, ...)) exceeds 16 MiB are
+ * rejected with QA_ERR_WORKSPACE.  The array is cleared by a fill kernel on
+ * `stream` at the first eager call on a device (a call captured before that
+ * carries the clear in its graph); every call returns the merge counters to
+ * zero.  All calls on one GPU share its array: calls that overlap on one GPU
+ * (another stream, another thread) race, so order them on one stream.
+ * Allocates nothing: no hipMalloc, hipFree or allocating library call.
+ */
+qa_status qa_decode_noalloc(const qa_cache* c, const qa_params* p, const void* q,
+                            const void* k, const void* v, const int32_t* positions,
+                            int batch, int max_ctx, void* out, float* lse,
+                            int32_t* dev_err, void* stream);
+
+/*
  * Exact verification of a block_len-token draft per sequence
  * ("dryft-flash-infer" agent guide, Where the wins are: speculative decoding
  * with exact verification).  Draft token i of sequence b sits at

@@ -344,6 +344,47 @@ qa_status qa_decode(const qa_cache* c, const qa_params* p, const void* q,
   return QA_OK;
 }
 
+qa_status qa_decode_noalloc(const qa_cache* c, const qa_params* p, const void* q,
+                            const void* k, const void* v, const int32_t* positions,
+                            int batch, int max_ctx, void* out, float* lse,
+                            int32_t* dev_err, void* stream) {
+  qa_status st = check_cache(c);
+  if (st != QA_OK) return st;
+  int G = 0;
+  st = check_params(p, c, &G);
+  if (st != QA_OK) return st;
+  QA_REQUIRE(q && k && v && out && positions, QA_ERR_NULL,
+             "q, k, v, out and positions must be non-NULL");
+  QA_REQUIRE(batch >= 1 && batch <= c->batch, QA_ERR_SHAPE,
+             "batch %d must be in [1, cache batch %d]", batch, c->batch);
+  QA_REQUIRE(max_ctx >= 1, QA_ERR_SHAPE, "max_ctx must be >= 1");
+  QA_REQUIRE(max_ctx <= c->capacity, QA_ERR_CAPACITY,
+             "max_ctx %d exceeds cache capacity %d", max_ctx, c->capacity);
+  QA_REQUIRE(al16(q) && al16(k) && al16(v) && al16(out) && al4(lse) && al4(positions) &&
+                 al4(dev_err),
+             QA_ERR_ALIGN, "q/k/v/out must be 16-byte aligned");
+  const qa::SplitLayout L = qa::decode_split_layout(batch, c->n_kv_heads, G, max_ctx);
+  const size_t cap_bytes = qa::noalloc_scratch_bytes();
+  QA_REQUIRE(L.total <= cap_bytes, QA_ERR_WORKSPACE,
+             "decode scratch of %zu bytes exceeds the library's %zu-byte array "
+             "(use qa_decode with a workspace)", L.total, cap_bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* scratch = nullptr;
+  hipError_t e = qa::noalloc_scratch(&scratch, s);
+  if (e != hipSuccess) return hip_fail(e, "decode scratch");
+  qa::DecodeArgs a;
+  fill_split_args(a, c, p, q, k, v, positions, batch, 1, max_ctx, out, lse, scratch,
+                  cap_bytes, L);
+  if (dev_err) a.err = dev_err;
+  int nk = 0;
+  e = qa::launch_decode(a, make_freq(p->rope_theta), G, s, &nk);
+  g_counters[CNT_KERNELS].fetch_add(nk);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  g_counters[CNT_DECODE].fetch_add(1);
+  g_last_error.clear();
+  return QA_OK;
+}
+
 qa_status qa_verify(const qa_cache* c, const qa_params* p, const void* q,
                     const void* k, const void* v, const int32_t* start_pos,
                     int batch, int block_len, int max_ctx, void* out,

@@ -172,6 +172,9 @@ hipError_t launch_verify(const DecodeArgs& a, const RopeFreq& f, int group,
                          hipStream_t s, int* n_kernels);
 hipError_t launch_merge(const DecodeArgs& a, int group, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+// qa_decode_noalloc's scratch array (noalloc.hip)
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** out, hipStream_t s);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 
 }  // namespace qa

@@ -22,7 +22,8 @@ HEAD_DIM = 128
 
 EXPORTS = (
     "qa_cache_alloc", "qa_cache_free", "qa_workspace_bytes",
-    "qa_workspace_init", "qa_prefill", "qa_decode", "qa_verify", "qa_copy",
+    "qa_workspace_init", "qa_prefill", "qa_decode", "qa_decode_noalloc",
+    "qa_verify", "qa_copy",
     "qa_rmsnorm_hidden",
     "qa_status_str", "qa_last_error", "qa_get_counters", "qa_reset_counters",
     "qa_device_error",
@@ -80,6 +81,8 @@ def lib():
                               _vp, _sz, _vp]),
         "qa_decode": (_i32, [P(QaCache), P(QaParams), _vp, _vp, _vp, _vp,
                              _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
+        "qa_decode_noalloc": (_i32, [P(QaCache), P(QaParams), _vp, _vp, _vp,
+                                     _vp, _i32, _i32, _vp, _vp, _vp, _vp]),
         "qa_verify": (_i32, [P(QaCache), P(QaParams), _vp, _vp, _vp, _vp,
                              _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
         "qa_copy": (_i32, [_vp, _vp, _sz, _vp]),
@@ -279,6 +282,32 @@ def decode(cache: Cache, params: Params, q, k, v, positions, max_ctx,
         _ptr(v), _ptr(positions), B, int(max_ctx), _ptr(out), _ptr(lse),
         _ptr(ws), ws.numel(), _stream(stream)))
     return out, lse, ws
+
+
+def decode_noalloc(cache: Cache, params: Params, q, k, v, positions, max_ctx,
+                   out, lse=None, dev_err=None, stream=None):
+    """qa_decode_noalloc: qa_decode on the library's own scratch array (no
+    workspace).  out must be given; dev_err is an optional int32 device
+    tensor that collects QA_DEVERR_* bits.  Returns out."""
+    Hq, Hkv = params.desc.n_q_heads, cache.n_kv_heads
+    B = q.shape[0]
+    _need(q, "q", torch.bfloat16, B * Hq * HEAD_DIM)
+    _need(k, "k", torch.bfloat16, B * Hkv * HEAD_DIM)
+    _need(v, "v", torch.bfloat16, B * Hkv * HEAD_DIM)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    _need(positions, "positions", torch.int32, B)
+    _need(out, "out", torch.bfloat16, B * Hq * HEAD_DIM)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, B * Hq)
+    if dev_err is not None:
+        _need(dev_err, "dev_err", torch.int32, 1)
+    _check(lib().qa_decode_noalloc(
+        ctypes.byref(cache.desc), ctypes.byref(params.desc), _ptr(q), _ptr(k),
+        _ptr(v), _ptr(positions), B, int(max_ctx), _ptr(out), _ptr(lse),
+        _ptr(dev_err), _stream(stream)))
+    return out
 
 
 def verify(cache: Cache, params: Params, q, k, v, start_pos, max_ctx,
