@@ -2,18 +2,20 @@
 //
 // "dryft-flash-infer" agent guide, Where the wins are: per-step overhead and
 // the preallocated, strided cache.  A workgroup owns (split, kv head,
-// sequence).  The cache rows before the new position are cut into near-equal
-// runs, one per split workgroup: it first issues all of its cache loads with
-// 16-byte loads, then, while they are in flight, forms q' for the G query
-// heads of the group.  Scores are a 16x16x32 bf16 MFMA (heads x keys, K
-// loaded straight into the B-operand layout); the softmax weights of key
-// pairs are packed as bf16x2 so P.V runs on dot2 instructions over the V rows
-// as loaded.  The four key groups of a wave are summed with lane swaps, the
-// four waves through LDS, and the workgroup writes a partial (max, sum,
-// unnormalised output).  One more workgroup per (sequence, kv head) handles
-// the new token alone: the K prologue (fp64, one RNE), the cache write, and
-// the one-key partial of the new slot.  It reads no cache rows and so runs
-// beside the streaming workgroups instead of lengthening one of them.
+// sequence); the cache rows before the new position are cut into near-equal
+// runs, one per split, and each of the four waves owns the 16-key tiles
+// w, w+4, ... of its run.  A workgroup first loads the small inputs (the
+// position, the q rows, and for split 0 the new token's k/v row) and waits
+// for them, so q' is formed while the cache bytes stream in rather than
+// after them; then it issues every cache load of its run at once (K straight
+// into the B-operand layout of the 16x16x32 bf16 MFMA, V as whole rows).
+// Each wave scores its own tiles (heads x keys), takes its own max, turns
+// its scores into weights and forms P.V with dot2 instructions over the V
+// rows as loaded, exchanging the weights through a per-wave LDS patch only;
+// the four waves' (max, sum, output) are combined once, after one barrier.
+// The new token's K prologue (fp64, one RNE), its cache write and its key
+// are folded into split 0: one wave runs the prologue while the cache loads
+// are in flight and adds the new key to its own softmax.
 //
 // When the pairs fill whole rounds of the 8-XCD deal (a.sync set), the
 // partials are merged inside the launch.  Workgroups are dealt to the XCDs
@@ -22,9 +24,9 @@
 // XCD's L2.  Each workgroup stores its partial, waits for the stores and
 // counts itself in on the pair's counter with a device-scope atomic; the last
 // one checks from the counter that the pair really shared an XCD, drops its
-// L1, reads the partials from L2, merges them in split order (the same
-// arithmetic as merge.hip) and returns the counter to zero.  Otherwise
-// merge.hip runs as a second launch.
+// L1, reads the partials from L2, merges them in split order (the arithmetic
+// of merge.hip) and returns the counter to zero.  Otherwise merge.hip runs
+// as a second launch.
 #include <utility>
 
 #include "qa.h"
@@ -56,25 +58,23 @@ __device__ __forceinline__ void rows4_sum(const float (&v)[N], float (&r)[N / 4]
   }
 }
 
-// Loads of the raw q rows of the heads w, w+4, ... of the group (elements
-// lane and lane+64), the norm weights and the rotation frequency of pair
-// `lane`.  Issued before any cache row, since the memory counter is waited on
-// in issue order.
+// The raw q rows of all G heads of the group (elements lane and lane+64 of
+// each), the norm weights and the rotation frequency of pair `lane`; every
+// wave forms q' for all heads itself, so no wave waits for another before
+// its first tile.
 template <int G>
 struct QRaw {
-  static constexpr int HPW = (G + 3) / 4;  // query heads per wave
-  uint16_t x0[HPW], x1[HPW];
+  uint16_t x0[G], x1[G];
   uint16_t w0, w1;
   double invf;
   __device__ __forceinline__ void load(const DecodeArgs& a, const RopeFreq& f, int b,
-                                       int g, int w, int lane) {
+                                       int g, int lane) {
     invf = f.inv_freq[lane];  // (a lane-indexed kernel-argument load)
 #pragma unroll
-    for (int i = 0; i < HPW; ++i) {
-      const int hl = min(w + 4 * i, G - 1);
-      const uint16_t* qr = a.q + ((size_t)b * a.n_q_heads + g * G + hl) * kHeadDim;
-      x0[i] = qr[lane];
-      x1[i] = qr[lane + 64];
+    for (int h = 0; h < G; ++h) {
+      const uint16_t* qr = a.q + ((size_t)b * a.n_q_heads + g * G + h) * kHeadDim;
+      x0[h] = qr[lane];
+      x1[h] = qr[lane + 64];
     }
     // loaded from a valid address whether or not weights are given, so no
     // branch sits between the loads
@@ -82,79 +82,47 @@ struct QRaw {
     w0 = wp[lane];
     w1 = wp[lane + 64];
   }
-  // q' = RoPE(RMSNorm(q) * w) * scale * log2(e), rounded to bf16 into s_q.
-  __device__ __forceinline__ void compute(const DecodeArgs& a, int pos, int w, int lane,
-                                          uint16_t (*s_q)[kHeadDim]) const {
-    float s32, c32;
-    sincos_reduced((double)pos * invf, &s32, &c32);
+  // q' = RoPE(RMSNorm(q) * w) * scale * log2(e) for every head, rounded to
+  // bf16 into the wave's patch sq.  The query side is rounded to bf16 for
+  // the MFMA, so fp32 suffices: the angle is reduced to whole turns in fp64
+  // and its cos/sin taken with the hardware's turn-based v_sin/v_cos; each
+  // head's sum of squares is a DPP sum within each 16-lane row plus the four
+  // row totals read from lanes 0, 16, 32, 48.
+  __device__ __forceinline__ void compute(const DecodeArgs& a, int pos, int lane,
+                                          uint16_t (*sq)[kHeadDim]) const {
+    const double turns = (double)pos * invf * 0.15915494309189535;  // / (2 pi)
+    const float fr = (float)(turns - floor(turns));
+    const float s32 = __builtin_amdgcn_sinf(fr), c32 = __builtin_amdgcn_cosf(fr);
     const float wf0 = a.q_norm_w ? bf_to_f(w0) : 1.f;
     const float wf1 = a.q_norm_w ? bf_to_f(w1) : 1.f;
+    float ss[G];
 #pragma unroll
-    for (int i = 0; i < HPW; ++i) {
-      const int hl = w + 4 * i;
-      if (hl >= G) break;
-      const float y0f = bf_to_f(x0[i]), y1f = bf_to_f(x1[i]);
-      const float ss = wave_sum(y0f * y0f + y1f * y1f);
-      const float rinv = 1.0f / sqrtf(ss * (1.0f / 128.0f) + (float)a.eps);
+    for (int h = 0; h < G; ++h) {
+      const float y0f = bf_to_f(x0[h]), y1f = bf_to_f(x1[h]);
+      ss[h] = row16_sum(y0f * y0f + y1f * y1f);
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float tot = (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(ss[h]), 0)) +
+                         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ss[h]), 16))) +
+                        (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(ss[h]), 32)) +
+                         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ss[h]), 48)));
+      const float y0f = bf_to_f(x0[h]), y1f = bf_to_f(x1[h]);
+      const float rinv = 1.0f / sqrtf(tot * (1.0f / 128.0f) + (float)a.eps);
       const float y0 = y0f * rinv * wf0, y1 = y1f * rinv * wf1;
       const uint32_t pk = pack_bf16x2((y0 * c32 - y1 * s32) * a.qscale,
                                       (y1 * c32 + y0 * s32) * a.qscale);
-      s_q[hl][lane] = (uint16_t)(pk & 0xffffu);
-      s_q[hl][lane + 64] = (uint16_t)(pk >> 16);
+      sq[h][lane] = (uint16_t)(pk & 0xffffu);
+      sq[h][lane + 64] = (uint16_t)(pk >> 16);
     }
   }
 };
 
-// The new token of sequence b, kv head g: k' (fp64, one RNE) and v written to
-// slot pos, and per query head the partial of that one key: m = q'.k',
-// l = 1, o = v.
-template <int G>
-__device__ __forceinline__ void new_token(const DecodeArgs& a, const RopeFreq& f, int b,
-                                          int g, int pos, bool ok, size_t rowbase,
-                                          uint16_t (*s_q)[kHeadDim], float* s_knew) {
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  if (!ok) {  // an invalid position writes nothing to the cache
-    if (tid < G) {
-      a.part_m[rowbase + tid] = -__builtin_inff();
-      a.part_l[rowbase + tid] = 0.f;
-    }
-    return;
-  }
-  const size_t pairidx = (size_t)b * a.n_kv_heads + g;
-  QRaw<G> qr;
-  qr.load(a, f, b, g, w, lane);
-  const uint16_t* kwp = a.k_norm_w ? a.k_norm_w : a.q;
-  const uint16_t kw0r = kwp[lane], kw1r = kwp[lane + 64];
-  const uint16_t* kr0 = a.k + pairidx * kHeadDim;
-  const uint16_t kx0 = kr0[lane], kx1 = kr0[lane + 64];
-  const uint32_t vx = reinterpret_cast<const uint32_t*>(a.v + pairidx * kHeadDim)[lane];
-  if (w == 0) {
-    double sn, cn;
-    sincos((double)pos * qr.invf, &sn, &cn);
-    uint16_t o0, o1;
-    const double wk0 = a.k_norm_w ? (double)bf_to_f(kw0r) : 1.0;
-    const double wk1 = a.k_norm_w ? (double)bf_to_f(kw1r) : 1.0;
-    kprime_pair(kx0, kx1, wk0, wk1, a.eps, cn, sn, &o0, &o1);
-    const size_t crow = (size_t)b * a.c.sb + (size_t)g * a.c.sh + (size_t)pos * a.c.sp;
-    a.c.k[crow + lane] = o0;
-    a.c.k[crow + lane + 64] = o1;
-    reinterpret_cast<uint32_t*>(a.c.v + crow)[lane] = vx;
-    s_knew[lane] = bf_to_f(o0);
-    s_knew[lane + 64] = bf_to_f(o1);
-  }
-  qr.compute(a, pos, w, lane, s_q);
-  __syncthreads();
-  for (int hl = w; hl < G; hl += 4) {
-    float d = bf_to_f(s_q[hl][lane]) * s_knew[lane] +
-              bf_to_f(s_q[hl][lane + 64]) * s_knew[lane + 64];
-    d = wave_sum(d);
-    *reinterpret_cast<float2*>(a.part_o + (rowbase + hl) * kHeadDim + 2 * lane) =
-        make_float2(bf_lo(vx), bf_hi(vx));
-    if (lane == 0) {
-      a.part_m[rowbase + hl] = d;
-      a.part_l[rowbase + hl] = 1.f;
-    }
-  }
+// Every lane of the wave sees what the wave wrote to LDS before this point.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // Buffer loads with sc0 miss the CU's L1 and are served by the XCD's L2,
@@ -204,7 +172,7 @@ __device__ __forceinline__ void merge_in_launch(const DecodeArgs& a, int pair, i
   const __amdgpu_buffer_rsrc_t rl = l2_rsrc(a.part_l + (size_t)pair * nrow, nrow * 4);
   const __amdgpu_buffer_rsrc_t ro =
       l2_rsrc(a.part_o + (size_t)pair * nrow * kHeadDim, nrow * kHeadDim * 4);
-  const MergeOut mo = merge_splits<32>((int)ns, [&](int s, float& m, float& l, float4& o) {
+  const MergeOut mo = merge_splits<8>((int)ns, [&](int s, float& m, float& l, float4& o) {
     const int row = s * G + hl;
     m = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rm, row * 4, 0, 1));
     l = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, row * 4, 0, 1));
@@ -216,199 +184,241 @@ __device__ __forceinline__ void merge_in_launch(const DecodeArgs& a, int pair, i
   store_merged(mo, bad, a.out + hrow * kHeadDim + d4, a.lse && d4 == 0 ? a.lse + hrow : nullptr);
 }
 
-// NT: 16-key tiles per split.  Tiles are scored in pairs (2m, 2m+1) so the
-// weights of keys k and k+16 pack into one bf16x2; wave w scores pairs
-// w, w+4, ...  Thread (kg, c) holds V rows kg + 16i (i < NT), dims 8c..8c+7.
-// Splits 0 .. n_split-2 stream the cache; split n_split-1 is the new token.
-template <int G, int NT>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a, RopeFreq f) {
-  constexpr int NP = (NT + 1) / 2;  // tile pairs
-  constexpr int PW = (NP + 3) / 4;  // tile pairs per wave (at most)
-  static_assert(NT >= 1 && NT <= kDecodeMaxTiles, "split length");
+// Position of key k (0..15) of a tile in the per-wave weight patch: lane
+// (kg, c) of the P.V step reads keys kg, kg+4, kg+8, kg+12 as one float4.
+__device__ __forceinline__ int pslot(int k) { return (k & 3) * 4 + (k >> 2); }
+
+// TPW: 16-key tiles per wave (a run is at most 16 * kDecodeWaves * TPW
+// rows); wave w owns the tiles w, w + kDecodeWaves, ... of its run.
+template <int G, int TPW>
+__global__ __launch_bounds__(64 * kDecodeWaves, 2) void decode_kernel(DecodeArgs a, RopeFreq f) {
+  constexpr int NW = kDecodeWaves;
+  static_assert(TPW >= 1 && TPW <= 4, "tiles per wave");
   static_assert(G <= 8, "group");
-  __shared__ __attribute__((aligned(16))) uint16_t s_q[G][kHeadDim];
-  __shared__ float s_max[4][8];
-  __shared__ float s_sum[4][8];
-  __shared__ __attribute__((aligned(16))) uint32_t s_pp[NP][16][8];
-  __shared__ __attribute__((aligned(16))) float s_red[4][G][kHeadDim];
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[NW][G][kHeadDim];
+  __shared__ __attribute__((aligned(16))) float s_p[NW][G][16];
+  __shared__ __attribute__((aligned(16))) float s_red[NW][G][kHeadDim];
+  __shared__ float s_m[NW][G], s_l[NW][G];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  // One-dimensional grid: the cache splits of every pair first, then the
-  // new-token workgroups, so the streaming workgroups are dealt out to the
-  // CUs evenly and the small ones fill in behind them.  With the in-launch
-  // merge, id 8 * (split * npair / 8 + k) + x is split `split` of pair
-  // x + 8k, so a pair's workgroups share id mod 8.
-  const int nc = a.n_split - 1;  // cache splits
+  const int ns = a.n_split;
   const int npair = a.batch * a.n_kv_heads;
   const int bid = blockIdx.x;
+  // One-dimensional grid.  With the in-launch merge, id
+  // 8 * (split * npair / 8 + k) + x is split `split` of pair x + 8k, so a
+  // pair's workgroups share id mod 8; otherwise pairs are contiguous.
   int pair, split;
   if (a.sync) {
     const int ppx = npair >> 3, idx = bid >> 3;
     split = idx / ppx;
     pair = (bid & 7) + 8 * (idx - split * ppx);
-  } else if (bid < npair * nc) {
-    pair = bid / nc;
-    split = bid - pair * nc;
   } else {
-    pair = bid - npair * nc;
-    split = nc;
+    pair = bid / ns;
+    split = bid - pair * ns;
   }
   const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads;
-  const int pos = a.positions[b];
-  const bool ok = pos >= 0 && pos < a.max_ctx;
-  if (!ok && split == 0 && g == 0 && tid == 0)
-    flag_error(a.err, QA_DEVERR_POSITION);
-  const size_t pairidx = (size_t)pair;
-  const size_t rowbase = (pairidx * a.n_split + split) * G;
+  const size_t rowbase = ((size_t)pair * ns + split) * G;
   const float ninf = -__builtin_inff();
-  do {  // every path ends at the merge below
-  if (split == nc) {
-    new_token<G>(a, f, b, g, pos, ok, rowbase, s_q, &s_red[0][0][0]);
-    break;
+  const bool nt_wave = split == 0 && w == NW - 1;  // the new token's prologue and key
+  const int kg = lane >> 4, c = lane & 15;
+  const int hrow = 4 * (lane >> 4);  // first head of this lane's score registers
+  uint16_t (*sq)[kHeadDim] = s_q[w];  // this wave's q'
+
+  // ---- 1. the small loads: the position (the cache loads wait for it),
+  // the q rows, and in the new token's wave its k/v row (V as dims
+  // 8c .. 8c+7, the layout of the P.V step) and the k norm weights
+  const int pos = a.positions[b];
+  QRaw<G> qr;
+  qr.load(a, f, b, g, lane);
+  uint16_t nk0 = 0, nk1 = 0, nw0 = 0, nw1 = 0;
+  u32x4 nv = {0u, 0u, 0u, 0u};
+  if (nt_wave) {
+    const uint16_t* kr = a.k + (size_t)pair * kHeadDim;
+    nk0 = kr[lane];
+    nk1 = kr[lane + 64];
+    const uint16_t* kwp = a.k_norm_w ? a.k_norm_w : a.q;
+    nw0 = kwp[lane];
+    nw1 = kwp[lane + 64];
+    nv = ld16(a.v + (size_t)pair * kHeadDim + 8 * c);
   }
-  // Cache rows [0, pos) -- everything before the new slot -- in nc
-  // near-equal runs, so every workgroup streams the same number of rows
-  // whatever the position; a run is at most ceil((max_ctx - 1) / nc) <= 16 NT
-  // rows (checked at launch).
+  const bool ok = pos >= 0 && pos < a.max_ctx;
+  if (!ok && split == 0 && g == 0 && tid == 0) flag_error(a.err, QA_DEVERR_POSITION);
+
+  // ---- 2. the cache tiles, two in flight ahead of the one being used.
+  // Rows [0, pos) -- all before the new slot -- in ns near-equal runs; keys
+  // past the run are clamped to its last row (read again, their scores
+  // masked), so every wave issues a fixed number of loads.  K: tile t, lane l
+  // holds dims 32 ks + 8 (l/16) .. +7 of key 16 t + l%16 (the B operand of
+  // k-step ks).  V: lane (kg, c) holds dims 8c .. 8c+7 of keys 16 t + kg + 4u.
   const int nrows = ok ? pos : 0;
-  const int k0 = (int)((long)split * nrows / nc);
-  const int k1 = (int)((long)(split + 1) * nrows / nc);
-  if (k0 >= k1) {  // nothing to attend in this split
-    if (tid < G) {
-      a.part_m[rowbase + tid] = ninf;
-      a.part_l[rowbase + tid] = 0.f;
-    }
-    break;
-  }
+  const int k0 = (int)((long)split * nrows / ns);
+  const int k1 = (int)((long)(split + 1) * nrows / ns);
+  const int klast = max(k1 - 1, 0);
   const uint16_t* kbase = a.c.k + (size_t)b * a.c.sb + (size_t)g * a.c.sh;
   const uint16_t* vbase = a.c.v + (size_t)b * a.c.sb + (size_t)g * a.c.sh;
-
-  // ---- 1. loads: the prologue's inputs first, then the cache rows.
-  QRaw<G> qr;
-  qr.load(a, f, b, g, w, lane);
-  __builtin_amdgcn_sched_barrier(0);  // the small loads stay first
-  // Rows past k1 are clamped to k1-1 (read again, their scores masked).
-  const int klast = k1 - 1;
-  // K, in the B-operand layout of the 16x16x32 MFMA: for tile t, lane l
-  // holds dims 32*ks + 8*(l/16) .. +7 of key 16*t + l%16.  Pairs past the
-  // split are skipped (a uniform branch); the odd tile past an odd NT is
-  // loaded clamped and its scores masked.
-  u32x4 kq[PW][2][4];
+  u32x4 kq[TPW][4], vr[TPW][4];
+  auto issue = [&](int i) {
+    const int t0 = k0 + 16 * (w + NW * i);
+    const uint16_t* kr = kbase + (size_t)min(t0 + (lane & 15), klast) * a.c.sp + 8 * kg;
 #pragma unroll
-  for (int i = 0; i < PW; ++i) {
-    const int m = w + 4 * i;
-    if ((i == 0 && NP >= 4) || m < NP) {
+    for (int ks = 0; ks < 4; ++ks) kq[i][ks] = ld16(kr + 32 * ks);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int key = min(k0 + 32 * m + 16 * j + (lane & 15), klast);
-        const uint16_t* kr = kbase + (size_t)key * a.c.sp + 8 * (lane >> 4);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) kq[i][j][ks] = ld16(kr + 32 * ks);
-      }
-    }
+    for (int u = 0; u < 4; ++u)
+      vr[i][u] = ld16(vbase + (size_t)min(t0 + kg + 4 * u, klast) * a.c.sp + 8 * c);
+  };
+  // q' for every head into the wave's patch (its inputs arrive with the
+  // position), ahead of the cache loads so that nothing after them waits
+  qr.compute(a, pos, lane, sq);
+  // the new token's k' (fp64, one RNE) into its slot, before this wave's
+  // own cache loads
+  float kn0 = 0.f, kn1 = 0.f;  // the new k' (bf16 values), elements lane, lane+64
+  if (nt_wave && ok) {
+    double sn, cn;
+    sincos((double)pos * qr.invf, &sn, &cn);
+    const double wk0 = a.k_norm_w ? (double)bf_to_f(nw0) : 1.0;
+    const double wk1 = a.k_norm_w ? (double)bf_to_f(nw1) : 1.0;
+    uint16_t o0, o1;
+    kprime_pair(nk0, nk1, wk0, wk1, a.eps, cn, sn, &o0, &o1);
+    const size_t crow = (size_t)b * a.c.sb + (size_t)g * a.c.sh + (size_t)pos * a.c.sp;
+    a.c.k[crow + lane] = o0;
+    a.c.k[crow + lane + 64] = o1;
+    if (kg == 0) st16(a.c.v + crow + 8 * c, nv);
+    kn0 = bf_to_f(o0);
+    kn1 = bf_to_f(o1);
   }
-  // V, for every thread: 8 dims (chunk c) of keys kg + 16*i.
-  const int kg = tid >> 4, c = tid & 15;
-  u32x4 vr[NT];
+  issue(0);
+  if (TPW > 1) issue(1);
+
+  // ---- 3. the new token's scores
+  wave_lds_sync();  // the wave's q' patch
+  float snew[G];
 #pragma unroll
-  for (int i = 0; i < NT; ++i) {
-    const int key = min(k0 + kg + 16 * i, klast);
-    vr[i] = ld16(vbase + (size_t)key * a.c.sp + 8 * c);
+  for (int h = 0; h < G; ++h) snew[h] = ninf;
+  if (nt_wave && ok) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      snew[h] = row16_sum(bf_to_f(sq[h][lane]) * kn0 + bf_to_f(sq[h][lane + 64]) * kn1);
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      snew[h] = (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(snew[h]), 0)) +
+                 __int_as_float(__builtin_amdgcn_readlane(__float_as_int(snew[h]), 16))) +
+                (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(snew[h]), 32)) +
+                 __int_as_float(__builtin_amdgcn_readlane(__float_as_int(snew[h]), 48)));
   }
-  // keep the loads in this order, ahead of the prologue arithmetic
-  __builtin_amdgcn_sched_barrier(0);
-
-  // ---- 2. q' while the cache loads are in flight
-  qr.compute(a, pos, w, lane, s_q);
-  __syncthreads();
-
-  // ---- 3. scores.  Wave w forms S = q' K^T for its tile pairs with the
-  // heads on the MFMA row axis: lane l holds head 4*(l/16) + r of key l%16.
-  const int hrow = 4 * (lane >> 4);  // first head of this lane's registers
-  f32x4 sj[PW][2];
+  u32x4 qv[4];  // the A operand: q' of head l%16, dims 32 ks + 8 (l/16) .. +7
   {
     const int qh = min(lane & 15, G - 1);
     const bool qvalid = (lane & 15) < G;
-    u32x4 qv[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      qv[ks] = ld16(&s_q[qh][32 * ks + 8 * (lane >> 4)]);
+      qv[ks] = ld16(&sq[qh][32 * ks + 8 * (lane >> 4)]);
       if (!qvalid) qv[ks] = u32x4{0u, 0u, 0u, 0u};
     }
-    float mx[4] = {ninf, ninf, ninf, ninf};
-#pragma unroll
-    for (int i = 0; i < PW; ++i) {
-      const int m = w + 4 * i;
-      if ((i == 0 && NP >= 4) || m < NP) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          sj[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks)
-            sj[i][j] = mfma16x16x32(qv[ks], kq[i][j][ks], sj[i][j]);
-          const bool kok = k0 + 32 * m + 16 * j + (lane & 15) < k1;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            if (!kok || hrow + r >= G) sj[i][j][r] = ninf;
-            mx[r] = fmaxf(mx[r], sj[i][j][r]);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float t = row16_max(mx[r]);
-      if ((lane & 15) == 0 && hrow + r < G) s_max[w][hrow + r] = t;
-    }
   }
-  __syncthreads();
 
-  // ---- 4. softmax weights: p = exp2(s - M) with M the split's max per head.
-  // Keys (k, k+16) of a tile pair are packed as bf16x2 for the P.V dot
-  // products.
+  // ---- 4. the wave's tiles in arrival order, online softmax: per head a
+  // running max m and sum l (wave-uniform), the output rescaled when m grows.
+  // Scores have the heads on the MFMA row axis (lane l: head 4 (l/16) + r of
+  // key l%16); the weights go through the wave's LDS patch to the P.V
+  // layout, where lane (kg, c) takes keys (kg, kg+8) and (kg+4, kg+12) of
+  // the tile as bf16 pairs for dot2.
+  float mrun[G], lrun[G];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int h = min(hrow + r, G - 1);
-    const float mh = fmaxf(fmaxf(s_max[0][h], s_max[1][h]), fmaxf(s_max[2][h], s_max[3][h]));
-    float sum = 0.f;
-#pragma unroll
-    for (int i = 0; i < PW; ++i) {
-      const int m = w + 4 * i;
-      if ((i == 0 && NP >= 4) || m < NP) {
-        const float p0 = __builtin_amdgcn_exp2f(sj[i][0][r] - mh);
-        const float p1 = __builtin_amdgcn_exp2f(sj[i][1][r] - mh);
-        sum += p0 + p1;
-        if (hrow + r < G) s_pp[m][lane & 15][hrow + r] = pack_bf16x2(p0, p1);
-      }
-    }
-    sum = row16_sum(sum);
-    if ((lane & 15) == 0 && hrow + r < G) s_sum[w][hrow + r] = sum;
+  for (int h = 0; h < G; ++h) {
+    mrun[h] = ninf;
+    lrun[h] = 0.f;
   }
-  __syncthreads();
-
-  // ---- 5. O += P.V: thread (kg, c) over its key pairs (kg + 32m, kg + 32m + 16)
   float acc[G * 8];
 #pragma unroll
   for (int n = 0; n < G * 8; ++n) acc[n] = 0.f;
 #pragma unroll
-  for (int m = 0; m < NP; ++m) {
-    uint32_t pp[G];
+  for (int i = 0; i < TPW; ++i) {
+    const int t0 = k0 + 16 * (w + NW * i);
+    if (t0 < k1) {  // (wave-uniform)
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int hl = 0; hl < G; ++hl) pp[hl] = s_pp[m][kg][hl];
+      for (int ks = 0; ks < 4; ++ks) sc = mfma16x16x32(qv[ks], kq[i][ks], sc);
+      const bool kok = t0 + (lane & 15) < k1;
+      float tm[4];
 #pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-      const uint32_t va = vr[2 * m][e2];
-      const uint32_t vb2 = 2 * m + 1 < NT ? vr[2 * m + 1 < NT ? 2 * m + 1 : 0][e2] : 0u;
-      const uint32_t lo = (va & 0xffffu) | (vb2 << 16);
-      const uint32_t hi = (va >> 16) | (vb2 & 0xffff0000u);
+      for (int r = 0; r < 4; ++r) {
+        sc[r] = (kok && hrow + r < G) ? sc[r] : ninf;
+        tm[r] = row16_max(sc[r]);
+      }
+      // the new running max and the factor for what was accumulated so far
+      // (key t0 is in the run, so every head's tile max is finite)
+      float mnew[G], alpha[G];
 #pragma unroll
-      for (int hl = 0; hl < G; ++hl) {
-        acc[8 * hl + 2 * e2] = dot2_bf16(pp[hl], lo, acc[8 * hl + 2 * e2]);
-        acc[8 * hl + 2 * e2 + 1] = dot2_bf16(pp[hl], hi, acc[8 * hl + 2 * e2 + 1]);
+      for (int h = 0; h < G; ++h) {
+        const float th = __int_as_float(
+            __builtin_amdgcn_readlane(__float_as_int(tm[h & 3]), 16 * (h >> 2)));
+        mnew[h] = fmaxf(mrun[h], th);
+        alpha[h] = mrun[h] == ninf ? 0.f : __builtin_amdgcn_exp2f(mrun[h] - mnew[h]);
+      }
+      float ps[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float mr = mnew[0];
+#pragma unroll
+        for (int h = 1; h < G; ++h) mr = hrow + r == h ? mnew[h] : mr;
+        const float pr = __builtin_amdgcn_exp2f(sc[r] - mr);
+        if (hrow + r < G) s_p[w][hrow + r][pslot(lane & 15)] = pr;
+        ps[r] = row16_sum(pr);
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float th = __int_as_float(
+            __builtin_amdgcn_readlane(__float_as_int(ps[h & 3]), 16 * (h >> 2)));
+        lrun[h] = lrun[h] * alpha[h] + th;
+        mrun[h] = mnew[h];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[8 * h + e] *= alpha[h];
+      }
+      wave_lds_sync();  // the weight patch
+      uint32_t pa[G], pb[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float4 pq = *reinterpret_cast<const float4*>(&s_p[w][h][4 * kg]);
+        pa[h] = pack_bf16x2(pq.x, pq.z);  // keys kg, kg+8
+        pb[h] = pack_bf16x2(pq.y, pq.w);  // keys kg+4, kg+12
+      }
+      wave_lds_sync();  // read before the next tile rewrites it
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const uint32_t v0 = vr[i][0][e2], v2 = vr[i][2][e2];
+        const uint32_t v1 = vr[i][1][e2], v3 = vr[i][3][e2];
+        const uint32_t lo02 = (v0 & 0xffffu) | (v2 << 16), hi02 = (v0 >> 16) | (v2 & 0xffff0000u);
+        const uint32_t lo13 = (v1 & 0xffffu) | (v3 << 16), hi13 = (v1 >> 16) | (v3 & 0xffff0000u);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          acc[8 * h + 2 * e2] = dot2_bf16(pa[h], lo02, acc[8 * h + 2 * e2]);
+          acc[8 * h + 2 * e2 + 1] = dot2_bf16(pa[h], hi02, acc[8 * h + 2 * e2 + 1]);
+          acc[8 * h + 2 * e2] = dot2_bf16(pb[h], lo13, acc[8 * h + 2 * e2]);
+          acc[8 * h + 2 * e2 + 1] = dot2_bf16(pb[h], hi13, acc[8 * h + 2 * e2 + 1]);
+        }
+      }
+    }
+    if (i + 2 < TPW) issue(i + 2);
+  }
+  // the new key: one more step of the online softmax (its weight in fp32),
+  // its value added once (key group 0)
+  if (nt_wave && ok) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mnew = fmaxf(mrun[h], snew[h]);
+      const float alpha = mrun[h] == ninf ? 0.f : __builtin_amdgcn_exp2f(mrun[h] - mnew);
+      const float pn = __builtin_amdgcn_exp2f(snew[h] - mnew);
+      lrun[h] = lrun[h] * alpha + pn;
+      mrun[h] = mnew;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        acc[8 * h + 2 * e2] = acc[8 * h + 2 * e2] * alpha + (kg == 0 ? pn * bf_lo(nv[e2]) : 0.f);
+        acc[8 * h + 2 * e2 + 1] =
+            acc[8 * h + 2 * e2 + 1] * alpha + (kg == 0 ? pn * bf_hi(nv[e2]) : 0.f);
       }
     }
   }
-  // the wave's four key groups, then the four waves
+  // the wave's four key groups, then its (max, sum, output) for the combine
   {
     float red[2 * G];
     rows4_sum<G * 8>(acc, red);
@@ -416,47 +426,64 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a, RopeFreq f) {
 #pragma unroll
     for (int j = 0; j < 2 * G; ++j)
       s_red[w][j >> 1][8 * c + 4 * (j & 1) + 2 * s16 + s32] = red[j];
+    if (lane == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        s_m[w][h] = mrun[h];
+        s_l[w][h] = lrun[h];
+      }
+    }
   }
   __syncthreads();
 
-  // ---- 6. the split's partial
+  // ---- 5. the split's partial: the waves combined at their common max
   if (tid < G * 32) {
     const int hl = tid >> 5, d4 = (tid & 31) * 4;
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    float m = ninf;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
-      const float4 t = *reinterpret_cast<const float4*>(&s_red[ww][hl][d4]);
-      o.x += t.x; o.y += t.y; o.z += t.z; o.w += t.w;
+    for (int ww = 0; ww < NW; ++ww) m = fmaxf(m, s_m[ww][hl]);
+    float l = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (m != ninf) {
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) {
+        const float mw = s_m[ww][hl];
+        const float wgt = mw == ninf ? 0.f : __builtin_amdgcn_exp2f(mw - m);
+        const float4 t = *reinterpret_cast<const float4*>(&s_red[ww][hl][d4]);
+        l += wgt * s_l[ww][hl];
+        o.x += wgt * t.x; o.y += wgt * t.y; o.z += wgt * t.z; o.w += wgt * t.w;
+      }
     }
     *reinterpret_cast<float4*>(a.part_o + (rowbase + hl) * kHeadDim + d4) = o;
     if ((tid & 31) == 0) {
-      a.part_m[rowbase + hl] =
-          fmaxf(fmaxf(s_max[0][hl], s_max[1][hl]), fmaxf(s_max[2][hl], s_max[3][hl]));
-      a.part_l[rowbase + hl] = (s_sum[0][hl] + s_sum[1][hl]) + (s_sum[2][hl] + s_sum[3][hl]);
+      a.part_m[rowbase + hl] = m;
+      a.part_l[rowbase + hl] = l;
     }
   }
-  } while (0);
   if (a.sync) merge_in_launch<G>(a, pair, b, g);
 }
 
-template <int G, int NT>
-static void launch_nt(const DecodeArgs& a, const RopeFreq& f, hipStream_t s) {
+template <int G, int TPW>
+static void launch_tpw(const DecodeArgs& a, const RopeFreq& f, hipStream_t s) {
   const dim3 grid(a.n_split * a.n_kv_heads * a.batch);
-  hipLaunchKernelGGL((decode_kernel<G, NT>), grid, dim3(256), 0, s, a, f);
+  hipLaunchKernelGGL((decode_kernel<G, TPW>), grid, dim3(64 * kDecodeWaves), 0, s, a, f);
 }
 
-template <int G, int... NT>
-static hipError_t launch_decode_g(const DecodeArgs& a, const RopeFreq& f,
-                                  hipStream_t s, std::integer_sequence<int, NT...>) {
+template <int G>
+static hipError_t launch_decode_g(const DecodeArgs& a, const RopeFreq& f, hipStream_t s) {
   const int nt = a.keys_per_split / 16;
-  if (a.keys_per_split % 16 != 0 || nt < 1 || nt > kDecodeMaxTiles || a.n_split < 2 ||
-      (long)(a.n_split - 1) * a.keys_per_split < a.max_ctx - 1)
+  if (a.keys_per_split % 16 != 0 || nt < 1 || nt > kDecodeMaxTiles || a.n_split < 1 ||
+      (long)a.n_split * a.keys_per_split < a.max_ctx - 1)
     return hipErrorInvalidValue;
-  ((nt == NT + 1 ? launch_nt<G, NT + 1>(a, f, s) : void()), ...);
+  switch ((nt + kDecodeWaves - 1) / kDecodeWaves) {
+    case 1: launch_tpw<G, 1>(a, f, s); break;
+    case 2: launch_tpw<G, 2>(a, f, s); break;
+    case 3: launch_tpw<G, 3>(a, f, s); break;
+    case 4: launch_tpw<G, 4>(a, f, s); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
-
-using kTiles = std::make_integer_sequence<int, kDecodeMaxTiles>;
 
 hipError_t launch_decode(const DecodeArgs& a, const RopeFreq& f, int group,
                          hipStream_t s, int* n_kernels) {
@@ -465,10 +492,10 @@ hipError_t launch_decode(const DecodeArgs& a, const RopeFreq& f, int group,
     return hipErrorInvalidValue;  // the grid numbering and the counter fields
   hipError_t e;
   switch (group) {
-    case 1: e = launch_decode_g<1>(a, f, s, kTiles{}); break;
-    case 2: e = launch_decode_g<2>(a, f, s, kTiles{}); break;
-    case 4: e = launch_decode_g<4>(a, f, s, kTiles{}); break;
-    case 8: e = launch_decode_g<8>(a, f, s, kTiles{}); break;
+    case 1: e = launch_decode_g<1>(a, f, s); break;
+    case 2: e = launch_decode_g<2>(a, f, s); break;
+    case 4: e = launch_decode_g<4>(a, f, s); break;
+    case 8: e = launch_decode_g<8>(a, f, s); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;

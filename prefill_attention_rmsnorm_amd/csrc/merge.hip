@@ -26,7 +26,7 @@ __global__ __launch_bounds__(128) void merge_kernel(DecodeArgs a, int G) {
   const float* pm = a.part_m + r0;
   const float* pl = a.part_l + r0;
   const float* po = a.part_o + r0 * kHeadDim + d4;
-  const MergeOut mo = merge_splits<32>(a.n_split, [&](int s, float& m, float& l, float4& o) {
+  const MergeOut mo = merge_splits<16>(a.n_split, [&](int s, float& m, float& l, float4& o) {
     m = pm[(size_t)s * rows];
     l = pl[(size_t)s * rows];
     o = *reinterpret_cast<const float4*>(po + (size_t)s * rows * kHeadDim);

@@ -131,9 +131,12 @@ __device__ __forceinline__ void sincos_reduced(double a, float* s, float* c) {
 // Log-sum-exp merge of n_split partial rows (m: max in log2 units, l: sum,
 // o: unnormalised output) for 4 consecutive dims of one row, in split order.
 // load(s, m, l, o) fetches split s's values; loads are issued CH splits at a
-// time so that a merge costs one memory round trip per CH splits.  Both
-// merge paths (the merge kernel and decode's in-launch merge) run this one
-// piece of arithmetic and differ only in how they load.
+// time (slots past n_split load split n_split - 1 again and count as empty)
+// so that a merge costs one memory round trip per CH splits, with no branch
+// between the loads or in the arithmetic.  A split with m = -inf is empty
+// and adds exactly zero (its o is not read into the sums).  Both merge paths
+// (the merge kernel and decode's in-launch merge) run this one piece of
+// arithmetic and differ only in how they load.
 struct MergeOut {
   float m, l;
   float4 o;
@@ -149,28 +152,25 @@ __device__ __forceinline__ MergeOut merge_splits(int n_split, Load&& load) {
     float mv[CH], lv[CH];
     float4 ov[CH];
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int s = s0 + c;
-      mv[c] = ninf;
-      lv[c] = 0.f;
-      ov[c] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (s < n_split) load(s, mv[c], lv[c], ov[c]);
-    }
+    for (int c = 0; c < CH; ++c) load(min(s0 + c, n_split - 1), mv[c], lv[c], ov[c]);
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+      if (s0 + c >= n_split) mv[c] = ninf;  // (a select, not a branch)
     float mc = ninf;
 #pragma unroll
     for (int c = 0; c < CH; ++c) mc = fmaxf(mc, mv[c]);
     const float mn = fmaxf(r.m, mc);
-    if (mn == ninf) continue;
     const float alpha = (r.m == ninf) ? 0.f : __builtin_amdgcn_exp2f(r.m - mn);
     r.l *= alpha;
     r.o.x *= alpha; r.o.y *= alpha; r.o.z *= alpha; r.o.w *= alpha;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      if (mv[c] == ninf) continue;
-      const float wgt = __builtin_amdgcn_exp2f(mv[c] - mn);
-      r.l += wgt * lv[c];
-      r.o.x += wgt * ov[c].x; r.o.y += wgt * ov[c].y;
-      r.o.z += wgt * ov[c].z; r.o.w += wgt * ov[c].w;
+      const bool empty = mv[c] == ninf;
+      const float wgt = empty ? 0.f : __builtin_amdgcn_exp2f(mv[c] - mn);
+      const float4 o = empty ? make_float4(0.f, 0.f, 0.f, 0.f) : ov[c];
+      r.l += wgt * (empty ? 0.f : lv[c]);
+      r.o.x += wgt * o.x; r.o.y += wgt * o.y;
+      r.o.z += wgt * o.z; r.o.w += wgt * o.w;
     }
     r.m = mn;
   }

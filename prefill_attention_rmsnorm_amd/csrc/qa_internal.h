@@ -36,16 +36,18 @@ struct SplitLayout {
   size_t sync_off = 0;  // decode only: the in-launch merge counters
 };
 
-// Decode: keys per split-K block, a multiple of 16 (one score tile) of at
-// most kDecodeMaxTiles tiles.  The split count aims at kDecodeBlocks
-// workgroups in all (two 256-thread workgroups per CU of a 256-CU part) and
-// does not pass it unless the split would exceed kDecodeMaxTiles, so every CU
-// streams the same number of cache bytes: a grid a few blocks over a multiple
-// of the CU count leaves those CUs a third block to stream after the rest
-// have finished.  The split is a function of the launch
-// sizes only (never of device-side positions), so graphs stay valid.
-constexpr int kDecodeBlocks = 512;
-constexpr int kDecodeMaxTiles = 16;
+// Decode: keys per split-K workgroup, a multiple of 16 (one score tile) of
+// at most kDecodeMaxTiles tiles.  A workgroup is kDecodeWaves waves (one
+// workgroup per CU at two waves per SIMD), and the split count aims at
+// kDecodeBlocks workgroups in all, so every CU streams the same number of
+// cache bytes in one round: a grid a few workgroups over a multiple of the
+// CU count leaves those CUs another workgroup to stream after the rest have
+// finished.  Fewer, larger workgroups also halve the partials the merge reads
+// against four-wave workgroups at two per CU.  The split is a function of the
+// launch sizes only (never of device-side positions), so graphs stay valid.
+constexpr int kDecodeWaves = 8;
+constexpr int kDecodeBlocks = 256;
+constexpr int kDecodeMaxTiles = 4 * kDecodeWaves;  // at most 4 tiles per wave
 inline int decode_keys_per_split(int batch, int n_kv, int max_ctx) {
   long pairs = (long)batch * n_kv;
   long want = kDecodeBlocks / pairs;  // splits per (sequence, kv head)
@@ -74,8 +76,8 @@ inline SplitLayout split_layout(int batch, int n_kv, int rows, int max_ctx,
   return L;
 }
 
-// Decode partials: the cache splits (rows before the new slot) and one for
-// the new token.  Then room for one 128-byte line per (sequence, kv head)
+// Decode partials: one per cache split (the rows before the new slot; split
+// 0 also takes the new token's key).  Then room for one 128-byte line per (sequence, kv head)
 // holding the arrival counter of the in-launch merge.  The counters are
 // placed from the END of the caller's workspace downwards (pair p at
 // end - 128 (p + 1), end = ws_bytes rounded down to 128), so a workspace
@@ -86,7 +88,7 @@ constexpr int kSyncWords = (int)(kSyncLine / 4);
 inline SplitLayout decode_split_layout(int batch, int n_kv, int G, int max_ctx) {
   const int rows_before = max_ctx > 1 ? max_ctx - 1 : 1;
   SplitLayout L = split_layout(batch, n_kv, G, rows_before,
-                               decode_keys_per_split(batch, n_kv, rows_before), 1);
+                               decode_keys_per_split(batch, n_kv, rows_before));
   L.sync_off = L.total;
   L.total = L.sync_off + round256((size_t)batch * n_kv * kSyncLine);
   return L;

@@ -21,27 +21,72 @@
 
 namespace qa {
 
+// Byte offset of the (cos, sin) of rotation pair i for draft token t in the
+// LDS table the query prologue reads (QPrologue::cs_from_lds): 512-byte rows,
+// 16-byte chunk c = i / 2 of row t at chunk position c ^ (t & 31).
+__device__ __forceinline__ uint32_t cs_lds_offset(int t, int i) {
+  return (uint32_t)(t * 512 + (((i >> 1) ^ (t & 31)) << 4) + ((i & 1) << 3));
+}
+
 template <int G, int NW>
 __global__ __launch_bounds__(NW * 64) void verify_kernel(DecodeArgs a, RopeFreq f) {
   constexpr int NT = NW * 64;
+  constexpr int kCsBytes = (128 / G) * 512;  // cos/sin rows of up to 128/G tokens
   __shared__ __attribute__((aligned(16))) unsigned char lds_k0[kKTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned char lds_k1[kKTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned char lds_v0[kKTileBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char lds_v1[kKTileBytes];
+  // V tile 1 and the queries' cos/sin rows share one array: the rows are
+  // read by the query prologue, which every wave finishes before the first
+  // barrier of attend(), and V tile 1 is first copied in after that barrier.
+  // (For G >= 4 the rows fit in the tile, and two workgroups fit per CU.)
+  __shared__ __attribute__((aligned(16)))
+  unsigned char lds_v1[kCsBytes > kKTileBytes ? kCsBytes : kKTileBytes];
   const AttnLds lds{lds_k0, lds_k1, lds_v0, lds_v1};
-  __shared__ __attribute__((aligned(16))) float2 cs[(128 / G) * kHalf];  // [draft token][pair]
+  unsigned char* lds_cs = lds_v1;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int j = l & 31, h2 = l >> 5;
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int n = a.block_len;
   const int rows = n * G;
+  const int n_old = a.n_split - 1;
+  const bool new_split = split == n_old;
+  const int r = 32 * w + j;
+  const bool row_ok = r < rows;
+  const int hl = row_ok ? r / n : 0, ti = row_ok ? r % n : 0;
+  const int h = g * G + hl;
+
+  // ---- loads that do not depend on the block's position go out first: the
+  // query row and its norm weights, and for the new slots' workgroup the
+  // first round of the block's k/v rows (token i = w + NW c of the block)
+  constexpr int CH = 8;  // new slots per round and wave
   const int L0 = a.positions[b];
+  QPrologue qp;
+  qp.load_qw(a.q + (((size_t)b * n + ti) * a.n_q_heads + h) * kHeadDim, row_ok, a.q_norm_w,
+             h2);
+  uint16_t kx0[CH], kx1[CH];
+  uint32_t vx[CH];
+  double wk0 = 1.0, wk1 = 1.0, invf = 0.0;
+  if (new_split) {
+    invf = f.inv_freq[l];
+    if (a.k_norm_w) {
+      wk0 = (double)bf_to_f(a.k_norm_w[l]);
+      wk1 = (double)bf_to_f(a.k_norm_w[l + 64]);
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int i = min(w + NW * c, n - 1);
+      const size_t src = (((size_t)b * n + i) * a.n_kv_heads + g) * kHeadDim;
+      kx0[c] = a.k[src + l];
+      kx1[c] = a.k[src + l + 64];
+      vx[c] = reinterpret_cast<const uint32_t*>(a.v + src)[l];
+    }
+  }
+
   const bool ok = L0 >= 0 && L0 + n <= a.max_ctx;
   if (!ok && split == 0 && g == 0 && tid == 0) flag_error(a.err, QA_DEVERR_POSITION);
-  const int n_old = a.n_split - 1;
   int k0, k1;
-  if (split < n_old) {  // tiles t0 .. t1-1 of the slots before the block
+  if (!new_split) {  // tiles t0 .. t1-1 of the slots before the block
     const int nt = ok ? (L0 + kKeyTile - 1) / kKeyTile : 0;
     const int t0 = (int)((long)split * nt / n_old);
     const int t1 = (int)((long)(split + 1) * nt / n_old);
@@ -53,44 +98,39 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(DecodeArgs a, RopeFreq 
   }
   const size_t pairidx = (size_t)b * a.n_kv_heads + g;
   const size_t rowbase = (pairidx * a.n_split + split) * rows;
-
-  const int r = 32 * w + j;
-  const bool row_ok = r < rows;
-  const int hl = row_ok ? r / n : 0, ti = row_ok ? r % n : 0;
-  const int h = g * G + hl;
   const int p = L0 + ti;
 
   if (k0 < k1) {
-    // ---- new slots owned by this split: k' (fp64) and v into the cache.
-    // Wave w takes slots nb0 + w, nb0 + w + NW, ...: all of a round's loads
-    // go out first, and the rotation advances from one slot to the next by
-    // the fp64 angle-addition identity (one turn by NW positions) instead
-    // of a fresh sincos per slot.
-    const int nb0 = max(k0, L0), nb1 = min(k1, L0 + n);
-    if (nb0 + w < nb1) {  // (wave-uniform)
-      constexpr int CH = 8;  // slots per round and wave
-      const double invf = f.inv_freq[l];
-      const double wk0 = a.k_norm_w ? (double)bf_to_f(a.k_norm_w[l]) : 1.0;
-      const double wk1 = a.k_norm_w ? (double)bf_to_f(a.k_norm_w[l + 64]) : 1.0;
+    const uint16_t* kbase = a.c.k + (size_t)b * a.c.sb + (size_t)g * a.c.sh;
+    const uint16_t* vbase = a.c.v + (size_t)b * a.c.sb + (size_t)g * a.c.sh;
+    TileLoader<NW> ld;
+    ld.init(__builtin_amdgcn_readfirstlane(w), l, a.c.sp);
+    // cache slots written by earlier calls: their first tiles can load now
+    if (!new_split) load_first(ld, lds, kbase, vbase, a.c.sp, k0, k1);
+
+    // ---- new slots: k' (fp64) and v into the cache.  Wave w takes slots
+    // L0 + w, L0 + w + NW, ...; the rotation advances from one slot to the
+    // next by the fp64 angle-addition identity (one turn by NW positions)
+    // instead of a fresh sincos per slot.
+    if (new_split && w < n) {  // (wave-uniform)
       double cn, sn, cstep, sstep;
-      sincos((double)(nb0 + w) * invf, &sn, &cn);
+      sincos((double)(L0 + w) * invf, &sn, &cn);
       sincos((double)NW * invf, &sstep, &cstep);
-      for (int base = nb0 + w; base < nb1; base += NW * CH) {
-        uint16_t kx0[CH], kx1[CH];
-        uint32_t vx[CH];
+      for (int i0 = w; i0 < n; i0 += NW * CH) {
+        if (i0 != w) {  // later rounds (blocks longer than NW * CH)
 #pragma unroll
-        for (int c = 0; c < CH; ++c) {
-          const int slot = min(base + NW * c, nb1 - 1);
-          const size_t src = (((size_t)b * n + (slot - L0)) * a.n_kv_heads + g) * kHeadDim;
-          kx0[c] = a.k[src + l];
-          kx1[c] = a.k[src + l + 64];
-          vx[c] = reinterpret_cast<const uint32_t*>(a.v + src)[l];
+          for (int c = 0; c < CH; ++c) {
+            const int i = min(i0 + NW * c, n - 1);
+            const size_t src = (((size_t)b * n + i) * a.n_kv_heads + g) * kHeadDim;
+            kx0[c] = a.k[src + l];
+            kx1[c] = a.k[src + l + 64];
+            vx[c] = reinterpret_cast<const uint32_t*>(a.v + src)[l];
+          }
         }
         // The slots' sums of squares are reduced across the wave together,
         // one butterfly step for all of them at a time, so their shuffle
-        // latencies overlap (one slot after the other, the chains made this
-        // workgroup the last of the launch).  Per slot the arithmetic is
-        // kprime_pair's: the same products and sums in the same order.
+        // latencies overlap.  Per slot the arithmetic is kprime_pair's: the
+        // same products and sums in the same order.
         double ss[CH];
         {
 #pragma clang fp contract(off)
@@ -106,20 +146,20 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(DecodeArgs a, RopeFreq 
         }
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-          const int slot = base + NW * c;
-          if (slot >= nb1) break;  // (wave-uniform)
+          const int i = i0 + NW * c;
+          if (i >= n) break;  // (wave-uniform)
           uint16_t o0, o1;
           {
 #pragma clang fp contract(off)
             const double x0 = (double)bf_to_f(kx0[c]), x1 = (double)bf_to_f(kx1[c]);
-            const double r = sqrt(ss[c] / 128.0 + a.eps);
-            const double y0 = x0 / r * wk0;
-            const double y1 = x1 / r * wk1;
+            const double rr = sqrt(ss[c] / 128.0 + a.eps);
+            const double y0 = x0 / rr * wk0;
+            const double y1 = x1 / rr * wk1;
             o0 = f64_to_bf16_rne(y0 * cn - y1 * sn);
             o1 = f64_to_bf16_rne(y1 * cn + y0 * sn);
           }
           const size_t crow =
-              (size_t)b * a.c.sb + (size_t)g * a.c.sh + (size_t)slot * a.c.sp;
+              (size_t)b * a.c.sb + (size_t)g * a.c.sh + (size_t)(L0 + i) * a.c.sp;
           a.c.k[crow + l] = o0;
           a.c.k[crow + l + 64] = o1;
           reinterpret_cast<uint32_t*>(a.c.v + crow)[l] = vx[c];
@@ -137,7 +177,8 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(DecodeArgs a, RopeFreq 
       sincos((double)L0 * f.inv_freq[l], &sb, &cb);
       sincos(f.inv_freq[l], &s1, &c1);
       for (int i = 0; i < n; ++i) {
-        cs[i * kHalf + l] = make_float2((float)cb, (float)sb);
+        *reinterpret_cast<float2*>(lds_cs + cs_lds_offset(i, l)) =
+            make_float2((float)cb, (float)sb);
         const double cn = cb * c1 - sb * s1;
         const double sn = sb * c1 + cb * s1;
         cb = cn;
@@ -146,21 +187,14 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(DecodeArgs a, RopeFreq 
     }
     __syncthreads();
     u32x4 qb[8];
-    {
-      QPrologue qp;
-      qp.load(a.q + (((size_t)b * n + ti) * a.n_q_heads + h) * kHeadDim,
-              row_ok && ok, cs + ti * kHalf, a.q_norm_w, h2);
-      qp.compute((float)a.eps, a.qscale, qb);
-    }
-    __syncthreads();  // cs and the new slots' cache writes are done
+    qp.cs_from_lds(lds_cs, ti, h2);
+    qp.compute((float)a.eps, a.qscale, qb);
+    // the new slots' cache writes are done before any wave copies them back
+    __syncthreads();
+    if (new_split) load_first(ld, lds, kbase, vbase, a.c.sp, k0, k1);
 
-    const uint16_t* kbase = a.c.k + (size_t)b * a.c.sb + (size_t)g * a.c.sh;
-    const uint16_t* vbase = a.c.v + (size_t)b * a.c.sb + (size_t)g * a.c.sh;
-    TileLoader<NW> ld;
-    ld.init(__builtin_amdgcn_readfirstlane(w), l, a.c.sp);
     WaveAttn st;
     st.init(l);
-    load_first(ld, lds, kbase, vbase, a.c.sp, k0, k1);
     const int lim_abs = row_ok ? min(p, k1 - 1) : k1 - 1;
     // tiles whose keys all lie below k1 and at or below the first draft
     // position need no mask

@@ -9,13 +9,27 @@ namespace qa {
 // before the block (near-equal runs of whole 64-key tiles, cut on the device
 // from the start position) and one more writes the block's slots and attends
 // to them alone, so its prologue is not followed by a long run of cache
-// tiles.  About one workgroup per CU in total (the MFMA kernel's registers
-// and LDS leave no room for a second); the split count is a function of the
-// launch sizes only.
-inline int verify_old_splits(int batch, int n_kv, int max_ctx, int block_len) {
-  long pairs = (long)batch * n_kv;
-  long want = pairs >= 128 ? 1 : 256 / pairs - 1;
-  long tiles = ((long)max_ctx - block_len + kKeyTile - 1) / kKeyTile;
+// tiles.  The workgroup count aims at filling every CU once: the MFMA
+// kernel's registers allow one wave per SIMD (so 4 / waves workgroups per
+// CU), and its LDS (three 16 KB tiles plus a fourth that also holds the
+// queries' cos/sin rows, 512 bytes per draft token) allows two workgroups
+// per CU when the rows fit in 16 KB (G >= 4), else one.  The split count is
+// a function of the launch sizes only.
+inline int verify_waves(int rows) { return rows <= 32 ? 1 : rows <= 64 ? 2 : 4; }
+
+inline int verify_workgroups_per_cu(int G, int block_len) {
+  const int by_simd = 4 / verify_waves(block_len * G);
+  const int by_lds = G >= 4 ? 2 : 1;
+  return by_simd < by_lds ? by_simd : by_lds;
+}
+
+constexpr int kVerifyCUs = 256;
+
+inline int verify_old_splits(int batch, int n_kv, int G, int max_ctx, int block_len) {
+  const long pairs = (long)batch * n_kv;
+  const long slots = (long)kVerifyCUs * verify_workgroups_per_cu(G, block_len);
+  long want = pairs * 2 > slots ? 1 : slots / pairs - 1;
+  const long tiles = ((long)max_ctx - block_len + kKeyTile - 1) / kKeyTile;
   if (want > tiles) want = tiles;
   return want < 1 ? 1 : (int)want;
 }
@@ -24,7 +38,7 @@ inline int verify_old_splits(int batch, int n_kv, int max_ctx, int block_len) {
 // used by verify).
 inline SplitLayout verify_split_layout(int batch, int n_kv, int G, int max_ctx,
                                        int block_len) {
-  const int n_old = verify_old_splits(batch, n_kv, max_ctx, block_len);
+  const int n_old = verify_old_splits(batch, n_kv, G, max_ctx, block_len);
   return split_layout(batch, n_kv, block_len * G, n_old, 1, 1);  // n_old + 1 splits
 }
 

@@ -183,3 +183,65 @@ def test_partly_right_drafter(model, prompts, greedy):
     _agree(spec, toks, logits, "partly right")
     assert all(l0 + N_NEW <= L < l0 + N_NEW + BLOCK
                for L, l0 in zip(lengths, LENS))
+
+
+@pytest.mark.parametrize("kind", ["partly_right", "random"])
+def test_oracle_replay_of_speculative_tokens(model, prompts, kind):
+    """The tokens the speculative loop emits, replayed teacher-forced through
+    the fp64 oracle ("dryft-flash-infer" agent guide, Invariants: each token is
+    the greedy choice on the engine's own prefix or within 2.0 logits of the
+    argmax there).  Sequence b's prompt and its emitted tokens but the last
+    form one oracle prefill (causal, so row t sees exactly the prefix up to
+    t); the oracle's LM-head logits at the row before each emitted token must
+    rank that token within 2.0 of the best."""
+    import oracle
+
+    from .gpu_helpers import EPS, THETA
+
+    g = np.random.default_rng(72 if kind == "random" else 73)
+    toks_g = None
+
+    def drafter(b, emitted, k):
+        if kind == "random":
+            return list(map(int, g.integers(0, model.V, k)))
+        # right for a random number of tokens (w.r.t. plain greedy), then wrong
+        i = len(emitted) + 1
+        d = (toks_g[b][i:i + k] + [0] * k)[:k]
+        cut = int(g.integers(0, k + 1))
+        return d[:cut] + [(t + 1) % model.V for t in d[cut:]]
+
+    if kind != "random":
+        cache, nxt = model.prefill(prompts)
+        toks_g = [[t] for t in nxt]  # a cheap greedy reference for the drafter
+        pos = np.array(LENS, dtype=np.int32)
+        ws = qa.workspace(qa.QA_OP_DECODE, len(prompts), model.Hq, model.Hkv,
+                          model.cap)
+        for _ in range(N_NEW - 1):
+            q, k, v = model.project([[t[-1]] for t in toks_g])
+            out, _, _ = qa.decode(cache, model.p, q[:, 0], k[:, 0], v[:, 0],
+                                  torch.from_numpy(pos).cuda(), model.cap, ws=ws)
+            for b, t in enumerate(model.head.gpu_tokens(out)):
+                toks_g[b].append(int(t))
+            pos = pos + 1
+    spec, _, _, calls = _run(model, prompts, drafter, f"replay {kind}")
+    exact, worst = 0, 0.0
+    for b, (prompt, emitted) in enumerate(zip(prompts, spec)):
+        seq_toks = list(prompt) + list(emitted[:-1])
+        q, k, v = model.project([[t] for t in seq_toks])
+        T = len(seq_toks)
+        oc = oracle.Cache.empty(1, model.Hkv, model.cap, 128)
+        cu, pos = W.packed_layout([T])
+        ref, _, _ = oracle.prefill(
+            oc, q.reshape(T, model.Hq, 128).cpu().double().numpy(),
+            k.reshape(T, model.Hkv, 128).cpu().double().numpy(),
+            v.reshape(T, model.Hkv, 128).cpu().double().numpy(), cu, pos,
+            scale=1.0 / np.sqrt(128), theta=THETA, eps=EPS)
+        rows = np.arange(len(prompt) - 1, T)  # predict emitted[0..N_NEW-1]
+        logits = model.head.ref_logits(ref[rows])
+        for lr, t in zip(logits, emitted):
+            gap = float(lr.max() - lr[int(t)])
+            worst = max(worst, gap)
+            exact += int(oracle.argmax_lowest(lr) == int(t))
+            assert oracle.margin_ok(lr, int(t), 2.0), f"seq {b}: token {t} {gap} below"
+    say(f"  replay {kind}: {exact}/{len(prompts) * N_NEW} exact argmax, worst gap "
+        f"{worst:.4f}, {calls} verify calls")
