@@ -167,45 +167,110 @@ def prefill_flops(B, Hq, S):
     return 2.0 * B * Hq * 128 * S * (S + 1)
 
 
-def cpu_baseline(budget_s=20.0):
-    """The fp64 oracle (as is) on a bounded sample of the same workload:
-    decode steps of the B=4, 2048-context layer shape, scaled to 36 layers."""
+def cpu_baseline(budget_s=10.0):
+    """The fp64 oracle (as is, never tuned) on bounded samples of the
+    workloads, on the host cores available to this process
+    (len(os.sched_getaffinity(0)) threads for the BLAS pool).
+
+    Headline leg: decode calls of the B=4, 2048-context layer shape, about
+    `budget_s` of work, scaled to a 36-layer step.  Further legs: one B=4 x
+    2048 prefill layer (the x36 figure is an extrapolation), one verify call
+    (B=4, 16-token block after 2048 slots), the tiny workload end to end
+    (64-token prefill + 8 decode steps), and one decode call on 1 thread."""
     import numpy as np
 
     import oracle
     import workloads as W
 
+    cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = 1
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+
+    def limit(n):
+        if threadpool_limits is None:
+            import contextlib
+            return contextlib.nullcontext()
+        return threadpool_limits(limits=n)
+
     w = W.get(2)
     B, Hq, Hkv, S, cap = w.batch, w.n_q_heads, w.n_kv_heads, 2048, w.capacity
-    c = oracle.Cache.empty(B, Hkv, cap, 128)
-    kk = W.normal_bf16((B, Hkv, S, 128), 2, 0, 0, "cache_k").double().numpy()
-    vv = W.normal_bf16((B, Hkv, S, 128), 2, 0, 0, "cache_v").double().numpy()
-    c.k[:, :, :S] = kk
-    c.v[:, :, :S] = vv
-    n = 0
-    t0 = time.perf_counter()
-    pos = np.full(B, S, dtype=np.int64)
-    while True:
+    kw = dict(scale=w.scale, theta=w.theta, eps=w.eps)
+
+    def seeded_cache(B_, Hkv_, L, cap_, seed):
+        c = oracle.Cache.empty(B_, Hkv_, cap_, 128)
+        c.k[:, :, :L] = W.normal_bf16((B_, Hkv_, L, 128), seed, 0, 0,
+                                      "cache_k").double().numpy()
+        c.v[:, :, :L] = W.normal_bf16((B_, Hkv_, L, 128), seed, 0, 0,
+                                      "cache_v").double().numpy()
+        return c
+
+    def decode_call(c, n, pos):
         q = W.normal_bf16((B, Hq, 128), 2, 1, n, "q").double().numpy()
         k = W.normal_bf16((B, Hkv, 128), 2, 1, n, "k").double().numpy()
         v = W.normal_bf16((B, Hkv, 128), 2, 1, n, "v").double().numpy()
-        _, _, c = oracle.decode(c, q, k, v, pos, scale=w.scale, theta=w.theta,
-                                eps=w.eps)
-        pos = pos + 1
-        n += 1
-        if time.perf_counter() - t0 > budget_s or n >= 64:
-            break
-    per_layer_us = (time.perf_counter() - t0) / n * 1e6
-    return {"value": per_layer_us * w.n_layers, "unit": "us/decode_step",
-            "cores": int(threads), "kind": "oracle",
+        t0 = time.perf_counter()
+        _, _, c = oracle.decode(c, q, k, v, pos, **kw)
+        return c, time.perf_counter() - t0
+
+    legs = {}
+    with limit(cores):
+        c = seeded_cache(B, Hkv, S, cap, 2)
+        n, spent, pos = 0, 0.0, np.full(B, S, dtype=np.int64)
+        while spent < budget_s and n < 64:
+            c, dt = decode_call(c, n, pos)
+            spent += dt
+            pos = pos + 1
+            n += 1
+        per_layer_us = spent / n * 1e6
+        # one prefill layer, B=4 x 2048
+        T = B * S
+        q = W.normal_bf16((T, Hq, 128), 2, 0, 0, "q").double().numpy()
+        k = W.normal_bf16((T, Hkv, 128), 2, 0, 0, "k").double().numpy()
+        v = W.normal_bf16((T, Hkv, 128), 2, 0, 0, "v").double().numpy()
+        cu, ppos = W.packed_layout([S] * B)
+        t0 = time.perf_counter()
+        oracle.prefill(oracle.Cache.empty(B, Hkv, cap, 128), q, k, v, cu, ppos, **kw)
+        legs["prefill_layer_us"] = round((time.perf_counter() - t0) * 1e6, 1)
+        legs["prefill_36_layers_us_extrapolated"] = round(legs["prefill_layer_us"] * 36, 1)
+        del q, k, v
+        # one verify call
+        w4 = W.get(4)
+        vc = seeded_cache(w4.batch, Hkv, w4.verify_start, w4.capacity, 4)
+        n_ = w4.verify_block
+        vq = W.normal_bf16((B, n_, Hq, 128), 4, 0, 0, "q").double().numpy()
+        vk = W.normal_bf16((B, n_, Hkv, 128), 4, 0, 0, "k").double().numpy()
+        vv = W.normal_bf16((B, n_, Hkv, 128), 4, 0, 0, "v").double().numpy()
+        t0 = time.perf_counter()
+        oracle.verify(vc, vq, vk, vv, [w4.verify_start] * B, **kw)
+        legs["verify_call_us"] = round((time.perf_counter() - t0) * 1e6, 1)
+        # the tiny workload: 64-token prefill, then 8 decode steps
+        w0 = W.get(0)
+        S0 = w0.prompt_lens[0]
+        tq = W.normal_bf16((S0, w0.n_q_heads, 128), 0, 0, 0, "q").double().numpy()
+        tk = W.normal_bf16((S0, w0.n_kv_heads, 128), 0, 0, 0, "k").double().numpy()
+        tv = W.normal_bf16((S0, w0.n_kv_heads, 128), 0, 0, 0, "v").double().numpy()
+        cu0, pos0 = W.packed_layout([S0])
+        t0 = time.perf_counter()
+        _, _, tc = oracle.prefill(oracle.Cache.empty(1, w0.n_kv_heads, w0.capacity, 128),
+                                  tq, tk, tv, cu0, pos0, **kw)
+        for st in range(w0.decode_steps):
+            dq = W.normal_bf16((1, w0.n_q_heads, 128), 0, 1, st, "q").double().numpy()
+            dk = W.normal_bf16((1, w0.n_kv_heads, 128), 0, 1, st, "k").double().numpy()
+            dv = W.normal_bf16((1, w0.n_kv_heads, 128), 0, 1, st, "v").double().numpy()
+            _, _, tc = oracle.decode(tc, dq, dk, dv, [S0 + st], **kw)
+        legs["tiny_run_us"] = round((time.perf_counter() - t0) * 1e6, 1)
+    with limit(1):
+        _, dt = decode_call(seeded_cache(B, Hkv, S, cap, 2), 0, np.full(B, S))
+        legs["decode_step_us_1_thread"] = round(dt * 1e6 * w.n_layers, 1)
+    return {"value": round(per_layer_us * w.n_layers, 1), "unit": "us/decode_step",
+            "cores": cores, "kind": "oracle",
             "sample": f"{n} single-layer decode calls at B=4, context "
                       f"{S + 1}..{S + n} (fp64 numpy oracle), scaled x{w.n_layers} "
-                      f"layers"}
+                      f"layers; legs: one prefill layer, one verify call, the "
+                      f"tiny run, one decode call on 1 thread (x{w.n_layers})",
+            "legs": legs}
 
 
 def ragged_spread(torch, qa, W, reps=15):
@@ -330,6 +395,192 @@ def rmsnorm_rate(torch, qa, reps=20):
     return {"tokens": T, "hidden": H, "us": round(us, 2),
             "algorithmic_bytes": nbytes, "GBps": round(gbps, 1),
             "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
+def _graph_time_us(torch, fn, reps=10, warm=2):
+    """Median time of one replay of a graph that captures fn(), with events
+    on the replaying stream (replays back to back, so no host enqueue gap
+    enters a sample)."""
+    import numpy as np
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(warm):
+        g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    return float(np.median(ts)), g
+
+
+def membw_probe(torch, qa, nbytes=1 << 30, reps=10):
+    """Plain device copy (qa_copy) of 1 GiB: read + write bytes over the
+    median time of 4 back-to-back copies in a graph."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+
+    def fn():
+        for _ in range(4):
+            qa.copy(src, dst)
+    us, _ = _graph_time_us(torch, fn, reps=reps)
+    gbps = 4 * 2 * nbytes / (us * 1e-6) / 1e9
+    del src, dst
+    return {"bytes_moved_per_copy": 2 * nbytes, "GBps": round(gbps, 1),
+            "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
+def verify_rotated(torch, qa, W, copies=8):
+    """The verify call on `copies` distinct caches (8 x 34 MB > the 256 MB
+    MALL), one graph of `copies` calls: per-call time with the cache bytes
+    coming from HBM."""
+    w4 = W.get(4)
+    B, Hq, Hkv, n, L0, cap = (w4.batch, w4.n_q_heads, w4.n_kv_heads,
+                              w4.verify_block, w4.verify_start, w4.capacity)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+
+    def rnd(*shape):
+        return torch.randn(*shape, generator=g, device="cuda").to(torch.bfloat16)
+    caches = []
+    for _ in range(copies):
+        c = qa.Cache.empty(B, Hkv, cap)
+        c.k[:, :, :L0] = rnd(B, Hkv, L0, 128)
+        c.v[:, :, :L0] = rnd(B, Hkv, L0, 128)
+        caches.append(c)
+    p = qa.Params(Hq, w4.scale, w4.theta, w4.eps)
+    q, k, v = rnd(B, n, Hq, 128), rnd(B, n, Hkv, 128), rnd(B, n, Hkv, 128)
+    start = torch.full((B,), L0, dtype=torch.int32, device="cuda")
+    out = torch.empty((B, n, Hq, 128), dtype=torch.bfloat16, device="cuda")
+    ws = qa.workspace(qa.QA_OP_VERIFY, B, Hq, Hkv, cap, n)
+
+    def fn():
+        for c in caches:
+            qa.verify(c, p, q, k, v, start, cap, out=out, ws=ws)
+    us, _ = _graph_time_us(torch, fn)
+    per = us / copies
+    nbytes = verify_bytes(B, Hq, Hkv, L0, n)
+    err = qa.device_error(ws)
+    return {"copies": copies, "us_per_call": round(per, 2),
+            "algorithmic_bytes": nbytes,
+            "GBps": round(nbytes / (per * 1e-6) / 1e9, 1),
+            "frac_hbm_peak": round(nbytes / (per * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "device_error": err}
+
+
+def verify_bytes(B, Hq, Hkv, L0, n):
+    """Algorithmic HBM bytes of one verify call: K/V of the L0 cached slots
+    read, the block's K/V written, q read and outputs written."""
+    return 2 * B * Hkv * L0 * 256 + 2 * B * n * Hkv * 256 + 2 * B * n * Hq * 256
+
+
+def small_latency(torch, qa, W):
+    """Latency of the two small workloads, each step replayed from a graph.
+
+    tiny: one 64-token prefill (4 query heads, 1 KV head) and 8 decode steps
+    whose positions advance on the device, as one graph (the whole run).
+    b1_s512: the B=1, 512-token prefill of one Qwen3-4B layer, and its 32
+    decode steps (positions advanced on the device) as one graph; its 2.2 MB
+    of cache stay in the caches, so only the time is reported."""
+    out = {}
+    g = torch.Generator(device="cuda")
+    g.manual_seed(6)
+
+    def rnd(*shape):
+        return torch.randn(*shape, generator=g, device="cuda").to(torch.bfloat16)
+    for key, idx in (("tiny", 0), ("b1_s512", 1)):
+        w = W.get(idx)
+        S, Hq, Hkv, cap, steps = (w.prompt_lens[0], w.n_q_heads, w.n_kv_heads,
+                                  w.capacity, w.decode_steps)
+        p = qa.Params(Hq, w.scale, w.theta, w.eps)
+        cache = qa.Cache.empty(1, Hkv, cap)
+        q, k, v = rnd(S, Hq, 128), rnd(S, Hkv, 128), rnd(S, Hkv, 128)
+        cu = torch.tensor([0, S], dtype=torch.int32, device="cuda")
+        pos = torch.arange(S, dtype=torch.int32, device="cuda")
+        pout = torch.empty((S, Hq, 128), dtype=torch.bfloat16, device="cuda")
+        pws = qa.workspace(qa.QA_OP_PREFILL, 1, Hq, Hkv, S)
+        dq, dk, dv = rnd(1, Hq, 128), rnd(1, Hkv, 128), rnd(1, Hkv, 128)
+        dpos = torch.full((1,), S, dtype=torch.int32, device="cuda")
+        dout = torch.empty((1, Hq, 128), dtype=torch.bfloat16, device="cuda")
+        dws = qa.workspace(qa.QA_OP_DECODE, 1, Hq, Hkv, cap)
+
+        def prefill():
+            qa.prefill(cache, p, q, k, v, cu, pos, S, out=pout, ws=pws)
+
+        def decode_steps():
+            dpos.fill_(S)
+            for _ in range(steps):
+                qa.decode(cache, p, dq, dk, dv, dpos, cap, out=dout, ws=dws)
+                dpos.add_(1)
+
+        t_pre, _ = _graph_time_us(torch, prefill)
+        t_dec, _ = _graph_time_us(torch, decode_steps)
+
+        def whole():
+            prefill()
+            decode_steps()
+        t_all, _ = _graph_time_us(torch, whole)
+        errs = qa.device_error(pws) | qa.device_error(dws)
+        out[key] = {"prompt": S, "decode_steps": steps,
+                    "prefill_us": round(t_pre, 2),
+                    "decode_us_per_step": round(t_dec / steps, 2),
+                    "run_us": round(t_all, 2), "device_error": errs}
+    return out
+
+
+def chunked_prefill(torch, qa, W):
+    """One B=4 x 2048 prefill layer in one call, and the same prompts in four
+    512-token chunks (each attending to the slots the earlier ones wrote):
+    the time to the last prompt token's output either way."""
+    w = W.get(2)
+    B, Hq, Hkv, S, cap, C = (w.batch, w.n_q_heads, w.n_kv_heads,
+                             w.prompt_lens[0], w.capacity, 512)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+
+    def rnd(*shape):
+        return torch.randn(*shape, generator=g, device="cuda").to(torch.bfloat16)
+    p = qa.Params(Hq, w.scale, w.theta, w.eps)
+    cache = qa.Cache.empty(B, Hkv, cap)
+    q, k, v = rnd(B * S, Hq, 128), rnd(B * S, Hkv, 128), rnd(B * S, Hkv, 128)
+    cu = torch.arange(0, B * S + 1, S, dtype=torch.int32, device="cuda")
+    pos = torch.arange(S, dtype=torch.int32, device="cuda").repeat(B)
+    out = torch.empty((B * S, Hq, 128), dtype=torch.bfloat16, device="cuda")
+    ws = qa.workspace(qa.QA_OP_PREFILL, B, Hq, Hkv, B * S)
+    chunks = []
+    for c0 in range(0, S, C):
+        idx = torch.cat([torch.arange(b * S + c0, b * S + c0 + C, device="cuda")
+                         for b in range(B)])
+        chunks.append((q[idx].contiguous(), k[idx].contiguous(),
+                       v[idx].contiguous(), pos[idx].contiguous(),
+                       torch.arange(0, B * C + 1, C, dtype=torch.int32,
+                                    device="cuda")))
+    cws = qa.workspace(qa.QA_OP_PREFILL, B, Hq, Hkv, B * C)
+    cout = torch.empty((B * C, Hq, 128), dtype=torch.bfloat16, device="cuda")
+
+    def one_shot():
+        qa.prefill(cache, p, q, k, v, cu, pos, S, out=out, ws=ws)
+
+    def chunked():
+        for cq, ck, cv, cp, ccu in chunks:
+            qa.prefill(cache, p, cq, ck, cv, ccu, cp, C, out=cout, ws=cws)
+    t1, _ = _graph_time_us(torch, one_shot)
+    t4, _ = _graph_time_us(torch, chunked)
+    return {"batch": B, "prompt": S, "chunk": C, "one_shot_us": round(t1, 2),
+            "chunked_us": round(t4, 2),
+            "device_error": qa.device_error(ws) | qa.device_error(cws)}
 
 
 def profile_kernels(wl, torch, qa):
@@ -514,6 +765,13 @@ def main():
         result["ragged_spread"] = ragged_spread(torch, qa, W)
         log("bench: hidden-state RMSNorm (untimed)")
         result["rmsnorm_hidden"] = rmsnorm_rate(torch, qa)
+        log("bench: membw probe, rotated verify, small workloads, chunked prefill")
+        probe = membw_probe(torch, qa)
+        probe["decode_frac_of_probe"] = round(dec_ach / probe["GBps"], 4)
+        result["membw_probe"] = probe
+        result["verify_rotated"] = verify_rotated(torch, qa, W)
+        result["latency_small"] = small_latency(torch, qa, W)
+        result["chunked_prefill"] = chunked_prefill(torch, qa, W)
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (fp64 oracle, bounded sample)")
         result["cpu_baseline"] = cpu_baseline()
