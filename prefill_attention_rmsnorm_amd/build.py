@@ -25,7 +25,7 @@ ARCH = "gfx950"
 SOURCES = ["qa_api.cpp", "util.hip", "prefill.hip", "decode.hip", "verify.hip",
            "merge.hip", "rmsnorm.hip", "noalloc.hip"]
 HEADERS = ["qa_internal.h", "qa_device.h", "attn_tile.h", "rmsnorm.h",
-           "verify_layout.h", "merge_count.h"]
+           "verify_layout.h", "merge_count.h", "merge_inline.h"]
 
 
 def hipcc() -> str:
@@ -82,11 +82,12 @@ def _write_build_info():
         "hipcc": ver[0] if ver else "",
         "arch": ARCH,
         "decode_source_sha": _sha(["decode.hip", "merge.hip", "qa_device.h",
-                                   "qa_internal.h", "merge_count.h"]),
+                                   "qa_internal.h", "merge_count.h", "merge_inline.h"]),
         "prefill_source_sha": _sha(["prefill.hip", "attn_tile.h",
                                     "qa_device.h", "qa_internal.h"]),
         "verify_source_sha": _sha(["verify.hip", "attn_tile.h", "qa_device.h",
-                                   "qa_internal.h", "verify_layout.h"]),
+                                   "qa_internal.h", "verify_layout.h", "merge_count.h",
+                                   "merge_inline.h", "merge.hip"]),
     }
     with open(os.path.join(BUILD, "BUILD_INFO.json"), "w") as f:
         json.dump(info, f, indent=1)

@@ -29,6 +29,7 @@
 // as a second launch.
 #include <utility>
 
+#include "merge_inline.h"
 #include "qa.h"
 #include "qa_device.h"
 
@@ -123,65 +124,6 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Buffer loads with sc0 miss the CU's L1 and are served by the XCD's L2,
-// where the other workgroups' stores of this launch have landed.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t l2_rsrc(const void* base, size_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes,
-                                           0x00020000);
-}
-
-// Called by every workgroup of the pair once its partial is stored.  Each
-// adds merge_count_add(d) to the pair's counter, d = (XCC_ID - id) mod 8:
-// the deal may start at any XCD, but a pair's workgroups share an XCD
-// exactly when they share d (merge_count.h).  A pair failing that is not
-// merged: its rows are zeroed and QA_DEVERR_MERGE is set.  An arriver that
-// finds a counter value no zeroed counter can reach (memory the counter
-// shares with other use, not cleared by qa_workspace_init) sets
-// QA_DEVERR_MERGE too; that pair's rows are then undefined.
-template <int G>
-__device__ __forceinline__ void merge_in_launch(const DecodeArgs& a, int pair, int b, int g) {
-  __shared__ int s_last, s_bad;
-  const int tid = threadIdx.x;
-  const unsigned ns = (unsigned)a.n_split;
-  unsigned* ctr = a.sync - kSyncWords * (pair + 1);
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are in L2
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned d = (__builtin_amdgcn_s_getreg((3 << 11) | 20) - blockIdx.x) & 7u;
-    const unsigned add = merge_count_add(d);  // HW_REG_XCC_ID above
-    const unsigned old =
-        __hip_atomic_fetch_add(ctr, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (!merge_count_valid(old, ns)) flag_error(a.err, QA_DEVERR_MERGE);
-    s_last = merge_count_last(old, ns);
-    s_bad = !merge_count_one_xcd(old + add, ns, d);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  asm volatile("buffer_inv sc0" ::: "memory");  // drop this CU's L1 lines
-  const bool bad = s_bad;
-  if (tid == 0) {
-    __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (bad) flag_error(a.err, QA_DEVERR_MERGE);
-  }
-  if (tid >= G * 32) return;
-  const int hl = tid >> 5, d4 = (tid & 31) * 4;
-  const size_t nrow = (size_t)ns * G;
-  const __amdgpu_buffer_rsrc_t rm = l2_rsrc(a.part_m + (size_t)pair * nrow, nrow * 4);
-  const __amdgpu_buffer_rsrc_t rl = l2_rsrc(a.part_l + (size_t)pair * nrow, nrow * 4);
-  const __amdgpu_buffer_rsrc_t ro =
-      l2_rsrc(a.part_o + (size_t)pair * nrow * kHeadDim, nrow * kHeadDim * 4);
-  const MergeOut mo = merge_splits<8>((int)ns, [&](int s, float& m, float& l, float4& o) {
-    const int row = s * G + hl;
-    m = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rm, row * 4, 0, 1));
-    l = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, row * 4, 0, 1));
-    const auto o4 = __builtin_amdgcn_raw_buffer_load_b128(ro, (row * kHeadDim + d4) * 4, 0, 1);
-    o = make_float4(__uint_as_float(o4[0]), __uint_as_float(o4[1]), __uint_as_float(o4[2]),
-                    __uint_as_float(o4[3]));
-  });
-  const size_t hrow = (size_t)b * a.n_q_heads + g * G + hl;
-  store_merged(mo, bad, a.out + hrow * kHeadDim + d4, a.lse && d4 == 0 ? a.lse + hrow : nullptr);
 }
 
 // Position of key k (0..15) of a tile in the per-wave weight patch: lane
@@ -460,7 +402,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 2) void decode_kernel(DecodeArgs
       a.part_l[rowbase + hl] = l;
     }
   }
-  if (a.sync) merge_in_launch<G>(a, pair, b, g);
+  if (a.sync) merge_pair<64 * kDecodeWaves, 1>(a, pair, b, g, G);
 }
 
 template <int G, int TPW>

@@ -141,40 +141,56 @@ struct MergeOut {
   float m, l;
   float4 o;
 };
+// IG rows at a time: load(j, s, m, l, o) fetches split s of row j; the loads
+// of all IG rows and CH splits are issued before any arithmetic.  Per row
+// the arithmetic is the same as for a single row.
+template <int CH, int IG, class Load>
+__device__ __forceinline__ void merge_splits_n(int n_split, Load&& load, MergeOut (&r)[IG]) {
+  const float ninf = -__builtin_inff();
+#pragma unroll
+  for (int j = 0; j < IG; ++j) {
+    r[j].m = ninf;
+    r[j].l = 0.f;
+    r[j].o = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  for (int s0 = 0; s0 < n_split; s0 += CH) {
+    float mv[IG][CH], lv[IG][CH];
+    float4 ov[IG][CH];
+#pragma unroll
+    for (int j = 0; j < IG; ++j)
+#pragma unroll
+      for (int c = 0; c < CH; ++c) load(j, min(s0 + c, n_split - 1), mv[j][c], lv[j][c], ov[j][c]);
+#pragma unroll
+    for (int j = 0; j < IG; ++j) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+        if (s0 + c >= n_split) mv[j][c] = ninf;  // (a select, not a branch)
+      float mc = ninf;
+#pragma unroll
+      for (int c = 0; c < CH; ++c) mc = fmaxf(mc, mv[j][c]);
+      const float mn = fmaxf(r[j].m, mc);
+      const float alpha = (r[j].m == ninf) ? 0.f : __builtin_amdgcn_exp2f(r[j].m - mn);
+      r[j].l *= alpha;
+      r[j].o.x *= alpha; r[j].o.y *= alpha; r[j].o.z *= alpha; r[j].o.w *= alpha;
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const bool empty = mv[j][c] == ninf;
+        const float wgt = empty ? 0.f : __builtin_amdgcn_exp2f(mv[j][c] - mn);
+        const float4 o = empty ? make_float4(0.f, 0.f, 0.f, 0.f) : ov[j][c];
+        r[j].l += wgt * (empty ? 0.f : lv[j][c]);
+        r[j].o.x += wgt * o.x; r[j].o.y += wgt * o.y;
+        r[j].o.z += wgt * o.z; r[j].o.w += wgt * o.w;
+      }
+      r[j].m = mn;
+    }
+  }
+}
 template <int CH, class Load>
 __device__ __forceinline__ MergeOut merge_splits(int n_split, Load&& load) {
-  const float ninf = -__builtin_inff();
-  MergeOut r;
-  r.m = ninf;
-  r.l = 0.f;
-  r.o = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < n_split; s0 += CH) {
-    float mv[CH], lv[CH];
-    float4 ov[CH];
-#pragma unroll
-    for (int c = 0; c < CH; ++c) load(min(s0 + c, n_split - 1), mv[c], lv[c], ov[c]);
-#pragma unroll
-    for (int c = 0; c < CH; ++c)
-      if (s0 + c >= n_split) mv[c] = ninf;  // (a select, not a branch)
-    float mc = ninf;
-#pragma unroll
-    for (int c = 0; c < CH; ++c) mc = fmaxf(mc, mv[c]);
-    const float mn = fmaxf(r.m, mc);
-    const float alpha = (r.m == ninf) ? 0.f : __builtin_amdgcn_exp2f(r.m - mn);
-    r.l *= alpha;
-    r.o.x *= alpha; r.o.y *= alpha; r.o.z *= alpha; r.o.w *= alpha;
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const bool empty = mv[c] == ninf;
-      const float wgt = empty ? 0.f : __builtin_amdgcn_exp2f(mv[c] - mn);
-      const float4 o = empty ? make_float4(0.f, 0.f, 0.f, 0.f) : ov[c];
-      r.l += wgt * (empty ? 0.f : lv[c]);
-      r.o.x += wgt * o.x; r.o.y += wgt * o.y;
-      r.o.z += wgt * o.z; r.o.w += wgt * o.w;
-    }
-    r.m = mn;
-  }
-  return r;
+  MergeOut r[1];
+  merge_splits_n<CH, 1>(
+      n_split, [&](int, int s, float& m, float& l, float4& o) { load(s, m, l, o); }, r);
+  return r[0];
 }
 
 // The merged row as bf16 output (4 dims) and natural-log LSE; a row with no

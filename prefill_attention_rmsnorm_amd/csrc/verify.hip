@@ -17,6 +17,7 @@
 // that workgroup ever reads the block's slots in this call, and the block
 // barrier orders its own writes before its reads.
 #include "attn_tile.h"
+#include "merge_inline.h"
 #include "qa.h"
 
 namespace qa {
@@ -46,7 +47,20 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(DecodeArgs a, RopeFreq 
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int j = l & 31, h2 = l >> 5;
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // One-dimensional grid.  With the in-launch merge, id
+  // 8 * (split * npair / 8 + k) + x is split `split` of pair x + 8k, so a
+  // pair's workgroups share id mod 8 (one XCD); otherwise pairs are contiguous.
+  const int npair = a.batch * a.n_kv_heads, bid = blockIdx.x;
+  int pair, split;
+  if (a.sync) {
+    const int ppx = npair >> 3, idx = bid >> 3;
+    split = idx / ppx;
+    pair = (bid & 7) + 8 * (idx - split * ppx);
+  } else {
+    pair = bid / a.n_split;
+    split = bid - pair * a.n_split;
+  }
+  const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads;
   const int n = a.block_len;
   const int rows = n * G;
   const int n_old = a.n_split - 1;
@@ -105,8 +119,6 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(DecodeArgs a, RopeFreq 
     const uint16_t* vbase = a.c.v + (size_t)b * a.c.sb + (size_t)g * a.c.sh;
     TileLoader<NW> ld;
     ld.init(__builtin_amdgcn_readfirstlane(w), l, a.c.sp);
-    // cache slots written by earlier calls: their first tiles can load now
-    if (!new_split) load_first(ld, lds, kbase, vbase, a.c.sp, k0, k1);
 
     // ---- new slots: k' (fp64) and v into the cache.  Wave w takes slots
     // L0 + w, L0 + w + NW, ...; the rotation advances from one slot to the
@@ -170,26 +182,25 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(DecodeArgs a, RopeFreq 
       }
     }
 
-    // ---- cos/sin of the draft positions for the queries (LDS, fp64
-    // rotation recurrence from the block start, stored as fp32)
-    if (w == 0) {
-      double sb, cb, s1, c1;
-      sincos((double)L0 * f.inv_freq[l], &sb, &cb);
-      sincos(f.inv_freq[l], &s1, &c1);
-      for (int i = 0; i < n; ++i) {
-        *reinterpret_cast<float2*>(lds_cs + cs_lds_offset(i, l)) =
-            make_float2((float)cb, (float)sb);
-        const double cn = cb * c1 - sb * s1;
-        const double sn = sb * c1 + cb * s1;
-        cb = cn;
-        sb = sn;
-      }
+    // ---- cos/sin of the draft positions for the queries (LDS), one entry
+    // per thread at a time: the angle reduced to whole turns in fp64, then
+    // the hardware's turn-based cos/sin (the queries are rounded to bf16
+    // for the MFMA, so fp32 suffices)
+    for (int e = tid; e < n * kHalf; e += NT) {
+      const int i = e >> 6, pi = e & (kHalf - 1);
+      const double turns = (double)(L0 + i) * f.inv_freq[pi] * 0.15915494309189535;
+      const float fr = (float)(turns - floor(turns));
+      *reinterpret_cast<float2*>(lds_cs + cs_lds_offset(i, pi)) =
+          make_float2(__builtin_amdgcn_cosf(fr), __builtin_amdgcn_sinf(fr));
     }
     __syncthreads();
     u32x4 qb[8];
     qp.cs_from_lds(lds_cs, ti, h2);
     qp.compute((float)a.eps, a.qscale, qb);
-    // the new slots' cache writes are done before any wave copies them back
+    // cache slots written by earlier calls: their first tiles load now, with
+    // q' already formed, so nothing but the copies stands before the first
+    // tile; the new slots' workgroup first orders its own cache writes
+    if (!new_split) load_first(ld, lds, kbase, vbase, a.c.sp, k0, k1);
     __syncthreads();
     if (new_split) load_first(ld, lds, kbase, vbase, a.c.sp, k0, k1);
 
@@ -222,13 +233,13 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(DecodeArgs a, RopeFreq 
       a.part_l[rowbase + rr] = 0.f;
     }
   }
-
+  if (a.sync) merge_pair<NT, 4>(a, pair, b, g, G);
 }
 
 template <int G>
 static hipError_t launch_verify_g(const DecodeArgs& a, const RopeFreq& f,
                                   hipStream_t s) {
-  const dim3 grid(a.n_split, a.n_kv_heads, a.batch);
+  const dim3 grid(a.n_split * a.n_kv_heads * a.batch);
   const int rows = a.block_len * G;
   if (rows <= 32)
     hipLaunchKernelGGL((verify_kernel<G, 1>), grid, dim3(64), 0, s, a, f);
@@ -244,6 +255,8 @@ static hipError_t launch_verify_g(const DecodeArgs& a, const RopeFreq& f,
 hipError_t launch_verify(const DecodeArgs& a, const RopeFreq& f, int group,
                          hipStream_t s, int* n_kernels) {
   *n_kernels = 0;
+  if (a.sync && ((a.batch * a.n_kv_heads) % 8 != 0 || a.n_split > kInlineMaxSplits))
+    return hipErrorInvalidValue;  // the grid numbering and the counter fields
   hipError_t e;
   switch (group) {
     case 1: e = launch_verify_g<1>(a, f, s); break;
@@ -254,6 +267,7 @@ hipError_t launch_verify(const DecodeArgs& a, const RopeFreq& f, int group,
   }
   if (e != hipSuccess) return e;
   *n_kernels = 1;
+  if (a.sync) return hipSuccess;  // merged inside the launch
   e = launch_merge(a, group, s);
   if (e == hipSuccess) *n_kernels = 2;
   return e;

@@ -24,10 +24,14 @@ inline int verify_workgroups_per_cu(int G, int block_len) {
 }
 
 constexpr int kVerifyCUs = 256;
+// Workgroups per CU the split count aims at (at most what fits).
+constexpr int kVerifyTargetPerCU = 1;
 
 inline int verify_old_splits(int batch, int n_kv, int G, int max_ctx, int block_len) {
   const long pairs = (long)batch * n_kv;
-  const long slots = (long)kVerifyCUs * verify_workgroups_per_cu(G, block_len);
+  const int fit = verify_workgroups_per_cu(G, block_len);
+  const long slots =
+      (long)kVerifyCUs * (fit < kVerifyTargetPerCU ? fit : kVerifyTargetPerCU);
   long want = pairs * 2 > slots ? 1 : slots / pairs - 1;
   const long tiles = ((long)max_ctx - block_len + kKeyTile - 1) / kKeyTile;
   if (want > tiles) want = tiles;
@@ -35,7 +39,10 @@ inline int verify_old_splits(int batch, int n_kv, int G, int max_ctx, int block_
 }
 
 // The old-slot splits' partials, then the block's (keys_per_split is not
-// used by verify).
+// used by verify).  The partials are merged by merge.hip in a second launch:
+// a verify partial is 64 rows of 130 floats per split, so one workgroup
+// reading a pair's partials back (as decode's in-launch merge does for its
+// 4 rows) would take longer than the second launch.
 inline SplitLayout verify_split_layout(int batch, int n_kv, int G, int max_ctx,
                                        int block_len) {
   const int n_old = verify_old_splits(batch, n_kv, G, max_ctx, block_len);
