@@ -33,6 +33,9 @@ Functions and what pins each of them (tests under ``tests/test_oracle_*``):
 ``rmsnorm_hidden``      hand values incl. a tie and the cast-placement case,
                         constant vectors, torch CPU bf16 add and the
                         float32 reference arithmetic
+``o_proj``,             hand values (a tie, the cast before the residual add),
+``attn_epilogue``       exact rational sums on small shapes, identity and
+                        zero weights, torch CPU bf16 linear layer
 ``lm_logits``           50-digit brute force on tiny shapes
 ``margin_ok``           rule cases (tie, exactly 2.0 below, just over)
 =====================  ====================================================
@@ -63,3 +66,4 @@ from .attention import (  # noqa: F401
     argmax_lowest,
 )
 from .rmsnorm_hidden import rmsnorm_hidden  # noqa: F401
+from .epilogue import o_proj, attn_epilogue  # noqa: F401

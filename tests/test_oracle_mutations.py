@@ -100,3 +100,47 @@ def test_planted_mistake_is_caught(monkeypatch, name, patch, pins):
         if hasattr(oracle, attr):
             monkeypatch.setattr(oracle, attr, fn)
     assert _run_all(pins) >= 1, f"no pin caught mutation {name}"
+
+
+# --- the attention epilogue (oracle/epilogue.py) -----------------------------
+
+import oracle.epilogue as E  # noqa: E402
+
+from . import test_oracle_epilogue as TE  # noqa: E402
+
+
+def _proj_not_rounded(o_flat, w_o):
+    return np.asarray(o_flat, dtype=np.float64) @ np.asarray(w_o, dtype=np.float64).T
+
+
+def _proj_weight_transposed(o_flat, w_o):
+    # the weight read as [in_dim, hidden] instead of one row per output
+    return A.bf16_round(np.asarray(o_flat, dtype=np.float64) @ np.asarray(w_o, dtype=np.float64))
+
+
+def _epilogue_norm_before_residual(o_flat, w_o, residual, weight=None, eps=1e-6):
+    h = E.o_proj(o_flat, w_o)
+    out, _ = E.rmsnorm_hidden(h, weight, eps)
+    r = A.bf16_round(np.asarray(residual, dtype=np.float64) + h)
+    return out, r, h
+
+
+EPILOGUE_MUTATIONS = [
+    ("projection_not_rounded", {"o_proj": _proj_not_rounded},
+     [_golden(TE.test_hand_values), TE.test_projection_equals_exact_rational_sum]),
+    ("projection_weight_transposed", {"o_proj": _proj_weight_transposed},
+     [TE.test_projection_equals_exact_rational_sum, TE.test_matches_torch_bf16_linear_layer]),
+    ("norm_before_residual", {"attn_epilogue": _epilogue_norm_before_residual},
+     [_golden(TE.test_hand_values), TE.test_identity_and_zero_weights]),
+]
+
+
+@pytest.mark.parametrize("name,patch,pins", EPILOGUE_MUTATIONS,
+                         ids=[m[0] for m in EPILOGUE_MUTATIONS])
+def test_planted_epilogue_mistake_is_caught(monkeypatch, name, patch, pins):
+    for attr, fn in patch.items():
+        monkeypatch.setattr(E, attr, fn)
+        monkeypatch.setattr(TE, attr, fn)
+        if hasattr(oracle, attr):
+            monkeypatch.setattr(oracle, attr, fn)
+    assert _run_all(pins) >= 1, f"no pin caught mutation {name}"
