@@ -256,6 +256,32 @@ qa_status qa_rmsnorm_hidden(const void* x, void* residual, const void* weight,
                             int n_tokens, int hidden, double eps, void* out,
                             void* stream);
 
+/*
+ * The attention epilogue of one decoder layer in the reference model's cast
+ * placement ("dryft-flash-infer" agent guide, Where the wins are: RMSNorm and
+ * the attention epilogue are small and safe to fuse; Numerics: sums may be
+ * reordered and accumulated in fp32, the bf16 casts may not move).  For each
+ * of n_tokens rows:
+ *   h        = bf16(o . w_o^T)              (output projection, fp32 sums)
+ *   residual = bf16(residual + h)           (updated in place)
+ *   out      = bf16(norm_w * bf16(residual / sqrt(mean(residual^2) + eps)))
+ * The last line is qa_rmsnorm_hidden's arithmetic on the new residual.
+ *   o        bf16 [n_tokens][in_dim], token stride o_tok_stride (elements;
+ *            the attention output with its heads concatenated, e.g. the
+ *            [T][n_q_heads][128] output of qa_prefill with in_dim = n_q_heads*128)
+ *   w_o      bf16 [hidden][in_dim]: the linear layer's weight, one row per
+ *            output feature
+ *   residual bf16 [n_tokens][hidden] (dense), read and overwritten
+ *   norm_w   bf16 [hidden] post-attention norm weight, or NULL for ones
+ *   out      bf16 [n_tokens][hidden] (dense), may not alias residual
+ * Requires in_dim a multiple of 64, hidden a multiple of 128 and at most
+ * 8192.  Two kernels (the projection GEMM, then the norm), asynchronous on
+ * `stream`, no allocation.  n_tokens == 0 is a valid no-op.
+ */
+qa_status qa_attn_epilogue(const void* o, int64_t o_tok_stride, const void* w_o,
+                           void* residual, const void* norm_w, int n_tokens, int in_dim,
+                           int hidden, double eps, void* out, void* stream);
+
 /* Plain device copy of `bytes` (multiple of 16) from src to dst on `stream`;
  * the calibration kernel for bandwidth and traffic measurements. */
 qa_status qa_copy(const void* src, void* dst, size_t bytes, void* stream);

@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libqa.so")
 ARCH = "gfx950"
 
 SOURCES = ["qa_api.cpp", "util.hip", "prefill.hip", "decode.hip", "verify.hip",
-           "merge.hip", "rmsnorm.hip", "noalloc.hip"]
+           "merge.hip", "rmsnorm.hip", "noalloc.hip", "epilogue.hip"]
 HEADERS = ["qa_internal.h", "qa_device.h", "attn_tile.h", "rmsnorm.h",
            "verify_layout.h", "merge_count.h", "merge_inline.h"]
 

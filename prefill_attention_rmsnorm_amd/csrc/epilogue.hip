@@ -1,0 +1,131 @@
+// Attention epilogue on gfx950: output projection with the residual add, then
+// the post-attention RMSNorm.
+//
+// "dryft-flash-infer" agent guide, Where the wins are: RMSNorm, rotary and
+// the attention epilogue are small and safe to fuse; Numerics: sums may be
+// reordered and accumulated in fp32, the bf16 casts stay where the reference
+// has them.  Kernel 1 is a bf16 MFMA GEMM, out[T][hidden] = o[T][in] .
+// w_o[hidden][in]^T with fp32 sums, whose epilogue rounds each sum to bf16
+// (the linear layer's output), adds the residual stream element and rounds
+// again (the bf16 residual add), writing the new residual in place.
+// Kernel 2 is the hidden-state RMSNorm of rmsnorm.hip on that residual.
+//
+// GEMM tiling: a workgroup of four waves owns a 128 x 128 output tile; K
+// advances 64 at a time through two LDS stages (register staged: the next
+// stage's global loads are issued before the current stage's MFMAs), each
+// 16-byte chunk c of a 128-byte LDS row r stored at chunk c ^ (r & 7) so the
+// operand reads of 32 rows hit distinct banks.  Wave (i, j) computes the
+// 64 x 64 quarter (i, j) as 2 x 2 blocks of v_mfma_f32_32x32x16_bf16, tokens
+// on the MFMA row axis and output features on the column axis, both operands
+// read with K contiguous (the linear layer's weight is [out][in]).
+#include "qa.h"
+#include "qa_device.h"
+#include "qa_internal.h"
+#include "rmsnorm.h"
+
+namespace qa {
+
+__device__ __forceinline__ uint32_t ep_swz(int row, int chunk) {
+  return (uint32_t)(row * 128 + ((chunk ^ (row & 7)) << 4));
+}
+
+__device__ __forceinline__ uint16_t f_to_bf(float x) {
+  return (uint16_t)(pack_bf16x2(x, 0.f) & 0xffffu);
+}
+
+__global__ __launch_bounds__(256) void epilogue_gemm_kernel(EpilogueArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char sA[2][kEpBM * 128];
+  __shared__ __attribute__((aligned(16))) unsigned char sB[2][kEpBN * 128];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int n0 = blockIdx.x * kEpBN, m0 = blockIdx.y * kEpBM;
+  const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
+
+  // 16-byte chunks tid + 256 j (j < 4) of each 128 x 64 stage: row id >> 3,
+  // chunk id & 7; token rows past the last are read from the last one (their
+  // results are not stored)
+  u32x4 ra[4], rb[4];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int id = tid + 256 * j, row = id >> 3, c = id & 7;
+      const int m = min(m0 + row, a.n_tokens - 1);
+      ra[j] = ld16(a.o + (size_t)m * a.o_stride + kt * kEpBK + 8 * c);
+      rb[j] = ld16(a.w + (size_t)(n0 + row) * a.in_dim + kt * kEpBK + 8 * c);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int id = tid + 256 * j, row = id >> 3, c = id & 7;
+      st16(sA[buf] + ep_swz(row, c), ra[j]);
+      st16(sB[buf] + ep_swz(row, c), rb[j]);
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = a.in_dim / kEpBK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+#pragma unroll
+    for (int ks = 0; ks < kEpBK / 16; ++ks) {
+      const int ch = 2 * ks + (l >> 5);
+      u32x4 av[2], bv[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        av[i] = *reinterpret_cast<const u32x4*>(sA[cur] + ep_swz(wm + 32 * i + (l & 31), ch));
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bv[j] = *reinterpret_cast<const u32x4*>(sB[cur] + ep_swz(wn + 32 * j + (l & 31), ch));
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(av[i], bv[j], acc[i][j]);
+    }
+    if (kt + 1 < nk) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: h = bf16(sum), r = bf16(h + residual), written over the residual
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + wn + 32 * j + (l & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+        if (row < a.n_tokens) {
+          uint16_t* rp = a.res + (size_t)row * a.hidden + col;
+          const float h = bf_to_f(f_to_bf(acc[i][j][r]));
+          *rp = f_to_bf(h + bf_to_f(*rp));
+        }
+      }
+    }
+}
+
+hipError_t launch_attn_epilogue(const EpilogueArgs& a, const NormArgs& n, hipStream_t s,
+                                int* n_kernels) {
+  *n_kernels = 0;
+  if (a.n_tokens == 0) return hipSuccess;
+  const dim3 grid(a.hidden / kEpBN, (a.n_tokens + kEpBM - 1) / kEpBM);
+  hipLaunchKernelGGL(epilogue_gemm_kernel, grid, dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  *n_kernels = 1;
+  e = launch_rmsnorm_hidden(n, s);
+  if (e == hipSuccess) *n_kernels = 2;
+  return e;
+}
+
+}  // namespace qa

@@ -450,6 +450,53 @@ qa_status qa_rmsnorm_hidden(const void* x, void* residual, const void* weight,
   return QA_OK;
 }
 
+qa_status qa_attn_epilogue(const void* o, int64_t o_tok_stride, const void* w_o,
+                           void* residual, const void* norm_w, int n_tokens, int in_dim,
+                           int hidden, double eps, void* out, void* stream) {
+  QA_REQUIRE(n_tokens >= 0, QA_ERR_SHAPE, "n_tokens %d < 0", n_tokens);
+  if (n_tokens == 0) {
+    g_last_error.clear();
+    return QA_OK;
+  }
+  QA_REQUIRE(o && w_o && residual && out, QA_ERR_NULL,
+             "o, w_o, residual and out must be non-NULL");
+  QA_REQUIRE(in_dim >= qa::kEpBK && in_dim % qa::kEpBK == 0, QA_ERR_UNSUPPORTED,
+             "in_dim %d must be a positive multiple of %d", in_dim, qa::kEpBK);
+  QA_REQUIRE(hidden >= qa::kEpBN && hidden % qa::kEpBN == 0, QA_ERR_UNSUPPORTED,
+             "hidden %d must be a positive multiple of %d", hidden, qa::kEpBN);
+  QA_REQUIRE(hidden <= 64 * 8 * qa::kNormMaxChunks, QA_ERR_UNSUPPORTED,
+             "hidden %d exceeds %d", hidden, 64 * 8 * qa::kNormMaxChunks);
+  QA_REQUIRE(o_tok_stride >= in_dim && o_tok_stride % 8 == 0, QA_ERR_SHAPE,
+             "o_tok_stride %lld must be >= in_dim and a multiple of 8",
+             (long long)o_tok_stride);
+  QA_REQUIRE(eps >= 0.0 && eps < 1.0e30, QA_ERR_SHAPE, "eps must be finite and >= 0");
+  QA_REQUIRE(al16(o) && al16(w_o) && al16(residual) && al16(norm_w) && al16(out),
+             QA_ERR_ALIGN, "o/w_o/residual/norm_w/out must be 16-byte aligned");
+  QA_REQUIRE(out != residual, QA_ERR_SHAPE, "out may not alias residual");
+  qa::EpilogueArgs a;
+  a.o = static_cast<const uint16_t*>(o);
+  a.o_stride = o_tok_stride;
+  a.w = static_cast<const uint16_t*>(w_o);
+  a.res = static_cast<uint16_t*>(residual);
+  a.n_tokens = n_tokens;
+  a.in_dim = in_dim;
+  a.hidden = hidden;
+  qa::NormArgs n;
+  n.x = static_cast<const uint16_t*>(residual);
+  n.res = nullptr;
+  n.w = static_cast<const uint16_t*>(norm_w);
+  n.out = static_cast<uint16_t*>(out);
+  n.n_tokens = n_tokens;
+  n.hidden = hidden;
+  n.eps = eps;
+  int nk = 0;
+  hipError_t e = qa::launch_attn_epilogue(a, n, static_cast<hipStream_t>(stream), &nk);
+  g_counters[CNT_KERNELS].fetch_add(nk);
+  if (e != hipSuccess) return hip_fail(e, "epilogue launch");
+  g_last_error.clear();
+  return QA_OK;
+}
+
 qa_status qa_copy(const void* src, void* dst, size_t bytes, void* stream) {
   QA_REQUIRE(src && dst, QA_ERR_NULL, "src/dst NULL");
   QA_REQUIRE(al16(src) && al16(dst) && bytes % 16 == 0, QA_ERR_ALIGN,

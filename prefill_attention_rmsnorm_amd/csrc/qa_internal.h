@@ -165,6 +165,17 @@ struct DecodeArgs {
                    // NULL: merge kernel
 };
 
+// Attention epilogue GEMM: 128 x 128 output tiles, K in steps of 64.
+constexpr int kEpBM = 128, kEpBN = 128, kEpBK = 64;
+
+struct EpilogueArgs {
+  const uint16_t* o;  // attention output [n_tokens][in_dim], token stride o_stride
+  int64_t o_stride;
+  const uint16_t* w;  // output projection weight [hidden][in_dim]
+  uint16_t* res;      // residual stream [n_tokens][hidden], updated in place
+  int n_tokens, in_dim, hidden;
+};
+
 // ---- launchers (return the hipError_t of the launch) ------------------------------
 hipError_t launch_prefill(const PrefillArgs& a, const RopeFreq& f, int group,
                           hipStream_t s, int* n_kernels);
@@ -174,6 +185,9 @@ hipError_t launch_verify(const DecodeArgs& a, const RopeFreq& f, int group,
                          hipStream_t s, int* n_kernels);
 hipError_t launch_merge(const DecodeArgs& a, int group, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+struct NormArgs;
+hipError_t launch_attn_epilogue(const EpilogueArgs& a, const NormArgs& n, hipStream_t s,
+                                int* n_kernels);
 // qa_decode_noalloc's scratch array (noalloc.hip)
 size_t noalloc_scratch_bytes();
 hipError_t noalloc_scratch(void** out, hipStream_t s);

@@ -24,7 +24,7 @@ EXPORTS = (
     "qa_cache_alloc", "qa_cache_free", "qa_workspace_bytes",
     "qa_workspace_init", "qa_prefill", "qa_decode", "qa_decode_noalloc",
     "qa_verify", "qa_copy",
-    "qa_rmsnorm_hidden",
+    "qa_rmsnorm_hidden", "qa_attn_epilogue",
     "qa_status_str", "qa_last_error", "qa_get_counters", "qa_reset_counters",
     "qa_device_error",
 )
@@ -88,6 +88,8 @@ def lib():
         "qa_copy": (_i32, [_vp, _vp, _sz, _vp]),
         "qa_rmsnorm_hidden": (_i32, [_vp, _vp, _vp, _i32, _i32, ctypes.c_double,
                                      _vp, _vp]),
+        "qa_attn_epilogue": (_i32, [_vp, _i64, _vp, _vp, _vp, _i32, _i32, _i32,
+                                    ctypes.c_double, _vp, _vp]),
         "qa_status_str": (ctypes.c_char_p, [_i32]),
         "qa_last_error": (ctypes.c_char_p, []),
         "qa_get_counters": (None, [P(ctypes.c_uint64)]),
@@ -365,6 +367,37 @@ def rmsnorm_hidden(x, residual=None, weight=None, eps=1e-6, out=None,
         _ptr(x), None if residual is None else _ptr(residual),
         None if weight is None else _ptr(weight), T, H, float(eps), _ptr(out),
         _stream(stream)))
+    return out
+
+
+def attn_epilogue(o, w_o, residual, norm_w=None, eps=1e-6, out=None,
+                  stream=None):
+    """qa_attn_epilogue: o bf16 [T, in_dim] (a token-strided view is fine,
+    e.g. a [T, Hq, 128] attention output reshaped), w_o bf16 [hidden, in_dim],
+    residual bf16 [T, hidden] (updated in place with bf16(residual + o w_o^T)),
+    norm_w bf16 [hidden] or None.  Returns out = the post-attention norm of the
+    new residual."""
+    if o.dim() == 3:
+        o = o.reshape(o.shape[0], -1)
+    if o.dim() != 2 or o.stride(1) != 1:
+        raise ValueError("o must be [T, in_dim] with a dense in_dim axis")
+    T, in_dim = o.shape
+    _need(o, "o", torch.bfloat16)
+    if w_o.dim() != 2 or w_o.shape[1] != in_dim or not w_o.is_contiguous():
+        raise ValueError("w_o must be a dense [hidden, in_dim] tensor")
+    hidden = w_o.shape[0]
+    _need(w_o, "w_o", torch.bfloat16)
+    if residual.shape != (T, hidden) or not residual.is_contiguous():
+        raise ValueError("residual must be a dense [T, hidden] tensor")
+    _need(residual, "residual", torch.bfloat16)
+    if norm_w is not None:
+        _need(norm_w, "norm_w", torch.bfloat16, hidden)
+    if out is None:
+        out = torch.empty_like(residual)
+    _need(out, "out", torch.bfloat16, T * hidden)
+    _check(lib().qa_attn_epilogue(
+        _ptr(o), o.stride(0), _ptr(w_o), _ptr(residual), _ptr(norm_w), T, in_dim,
+        hidden, float(eps), _ptr(out), _stream(stream)))
     return out
 
 
