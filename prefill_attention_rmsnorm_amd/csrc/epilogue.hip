@@ -18,6 +18,16 @@
 // 64 x 64 quarter (i, j) as 2 x 2 blocks of v_mfma_f32_32x32x16_bf16, tokens
 // on the MFMA row axis and output features on the column axis, both operands
 // read with K contiguous (the linear layer's weight is [out][in]).
+//
+// Decode-sized batches (at most kEpSmallT tokens) take a second kernel: the
+// GEMM grid would be a few tiles wide there, while the work is one streaming
+// read of w_o.  A workgroup owns kEpSmallN output features and its eight waves
+// split K into eighths; each lane holds its wave's slice of those weight rows
+// in registers (all loads in flight at once), token tiles of 16 run
+// v_mfma_f32_16x16x32_bf16 over them (tokens on the row axis, the 16
+// features on the column axis), and the eight
+// partial sums of an output are added in wave order through LDS, so the
+// result does not depend on timing.
 #include "qa.h"
 #include "qa_device.h"
 #include "qa_internal.h"
@@ -114,12 +124,79 @@ __global__ __launch_bounds__(256) void epilogue_gemm_kernel(EpilogueArgs a) {
     }
 }
 
+template <int KS>
+__global__ __launch_bounds__(512) void epilogue_small_kernel(EpilogueArgs a) {
+  static_assert(kEpSmallN == 16, "one feature per MFMA column");
+  __shared__ float part[8][16][kEpSmallN + 1];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int n0 = blockIdx.x * kEpSmallN;
+  const int kw = w * (32 * KS);  // this wave's K range: kw .. kw + 32 KS - 1
+  const int kq = 8 * (l >> 4);   // the lane's 8 k values within a 32-wide step
+  // B operand of step s: W[n0 + (l & 15)][kw + 32 s + kq .. +7]
+  u32x4 wb[KS];
+  const uint16_t* wrow = a.w + (size_t)(n0 + (l & 15)) * a.in_dim + kw + kq;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) wb[s] = ld16(wrow + 32 * s);
+  // the residual element each of the first 256 threads adds to, read now so
+  // that its latency overlaps the weight stream (the next tile's is read
+  // after this tile's store)
+  const int tr = tid / kEpSmallN, f = tid % kEpSmallN;
+  uint16_t* rp = a.res + (size_t)min(tr, a.n_tokens - 1) * a.hidden + n0 + f;
+  uint16_t rv = tid < 16 * kEpSmallN ? *rp : (uint16_t)0;
+  for (int t0 = 0; t0 < a.n_tokens; t0 += 16) {
+    const int tt = min(t0 + (l & 15), a.n_tokens - 1);  // rows past the last repeat it
+    const uint16_t* orow = a.o + (size_t)tt * a.o_stride + kw + kq;
+    u32x4 ob[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) ob[s] = ld16(orow + 32 * s);
+    // all KS loads in flight before the first MFMA: left alone, the compiler
+    // pipelines them two deep, and each MFMA then waits a round trip to L2
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) acc = mfma16x16x32(ob[s], wb[s], acc);
+    // D: lane l holds tokens t0 + 4 (l >> 4) + r of feature column l & 15
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part[w][4 * (l >> 4) + r][l & 15] = acc[r];
+    __syncthreads();
+    if (tid < 16 * kEpSmallN) {
+      const int tok = t0 + tr;
+      float sum = part[0][tr][f];
+#pragma unroll
+      for (int v = 1; v < 8; ++v) sum += part[v][tr][f];
+      if (tok < a.n_tokens) {
+        const float h = bf_to_f(f_to_bf(sum));
+        *rp = f_to_bf(h + bf_to_f(rv));
+      }
+      if (tok + 16 < a.n_tokens) {
+        rp += (size_t)16 * a.hidden;
+        rv = *rp;
+      }
+    }
+    __syncthreads();  // part is rewritten by the next token tile
+  }
+}
+
 hipError_t launch_attn_epilogue(const EpilogueArgs& a, const NormArgs& n, hipStream_t s,
                                 int* n_kernels) {
   *n_kernels = 0;
   if (a.n_tokens == 0) return hipSuccess;
-  const dim3 grid(a.hidden / kEpBN, (a.n_tokens + kEpBM - 1) / kEpBM);
-  hipLaunchKernelGGL(epilogue_gemm_kernel, grid, dim3(256), 0, s, a);
+  const int ks = a.in_dim / 256;  // K steps of 32 per wave on the small path
+  const bool small = a.n_tokens <= kEpSmallT && a.in_dim % 256 == 0 &&
+                     (ks == 2 || ks == 4 || ks == 8 || ks == 16 || ks == 32);
+  if (small) {
+    const dim3 grid(a.hidden / kEpSmallN);
+    switch (ks) {
+      case 2: hipLaunchKernelGGL(epilogue_small_kernel<2>, grid, dim3(512), 0, s, a); break;
+      case 4: hipLaunchKernelGGL(epilogue_small_kernel<4>, grid, dim3(512), 0, s, a); break;
+      case 8: hipLaunchKernelGGL(epilogue_small_kernel<8>, grid, dim3(512), 0, s, a); break;
+      case 16: hipLaunchKernelGGL(epilogue_small_kernel<16>, grid, dim3(512), 0, s, a); break;
+      default: hipLaunchKernelGGL(epilogue_small_kernel<32>, grid, dim3(512), 0, s, a); break;
+    }
+  } else {
+    const dim3 grid(a.hidden / kEpBN, (a.n_tokens + kEpBM - 1) / kEpBM);
+    hipLaunchKernelGGL(epilogue_gemm_kernel, grid, dim3(256), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   *n_kernels = 1;

@@ -165,8 +165,11 @@ struct DecodeArgs {
                    // NULL: merge kernel
 };
 
-// Attention epilogue GEMM: 128 x 128 output tiles, K in steps of 64.
+// Attention epilogue GEMM: 128 x 128 output tiles, K in steps of 64.  Up to
+// kEpSmallT tokens use the streaming kernel instead: kEpSmallN output features
+// per workgroup.
 constexpr int kEpBM = 128, kEpBN = 128, kEpBK = 64;
+constexpr int kEpSmallT = 32, kEpSmallN = 16;
 
 struct EpilogueArgs {
   const uint16_t* o;  // attention output [n_tokens][in_dim], token stride o_stride

@@ -11,6 +11,8 @@ namespace qa {
 // 64 * 8 * kNormMaxChunks (one wave per row, kNormMaxChunks 16-byte pieces
 // per lane).
 constexpr int kNormMaxChunks = 16;
+// Batches up to this many rows run one workgroup per row.
+constexpr int kNormRowTokens = 512;
 
 struct NormArgs {
   const uint16_t* x;

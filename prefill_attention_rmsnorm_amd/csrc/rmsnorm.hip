@@ -17,7 +17,8 @@
 // One wave per token row: all loads of the row first (CH 16-byte pieces per
 // lane, CH = ceil(hidden / 512), a template argument so that registers are
 // sized for the row at hand), the sum of squares reduced across the wave,
-// then the row written back.  The traffic is 2 bytes per element for each of
+// then the row written back.  Batches of at most kNormRowTokens rows spread
+// each row over a workgroup instead (rmsnorm_row_kernel).  The traffic is 2 bytes per element for each of
 // x, residual in, out and residual out; at the measured rate the per-element
 // fp64 arithmetic and roundings (a few dozen instructions), not the bytes,
 // set the time.
@@ -49,6 +50,43 @@ __device__ __forceinline__ uint16_t half_of(const u32x4& v, int e) {
   return (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
 }
 
+// The 8 values of one 16-byte piece: r = bf16(x + residual) (r = x without
+// a residual), their squares added to ss.
+__device__ __forceinline__ u32x4 add_piece(u32x4 x, u32x4 res, bool has_res, double& ss) {
+  u32x4 out;
+#pragma unroll
+  for (int e2 = 0; e2 < 4; ++e2) {
+    uint16_t r[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint16_t xb = half_of(x, 2 * e2 + h);
+      r[h] = has_res ? rne_bf16((double)bf_to_f(xb) + (double)bf_to_f(half_of(res, 2 * e2 + h)))
+                     : xb;
+      const double rv = (double)bf_to_f(r[h]);
+      ss += rv * rv;
+    }
+    out[e2] = (uint32_t)r[0] | ((uint32_t)r[1] << 16);
+  }
+  return out;
+}
+
+// out = bf16(w * bf16(r / s)) (no weight: bf16(r / s)) for the 8 values of a piece.
+__device__ __forceinline__ u32x4 norm_piece(u32x4 r, u32x4 w, bool has_w, double s) {
+  u32x4 o;
+#pragma unroll
+  for (int e2 = 0; e2 < 4; ++e2) {
+    uint16_t ob[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int e = 2 * e2 + h;
+      const uint16_t yb = rne_bf16((double)bf_to_f(half_of(r, e)) / s);
+      ob[h] = has_w ? rne_bf16((double)bf_to_f(half_of(w, e)) * (double)bf_to_f(yb)) : yb;
+    }
+    o[e2] = (uint32_t)ob[0] | ((uint32_t)ob[1] << 16);
+  }
+  return o;
+}
+
 template <int CH>
 __global__ __launch_bounds__(256) void rmsnorm_hidden_kernel(NormArgs a) {
   const int lane = threadIdx.x & 63;
@@ -70,19 +108,7 @@ __global__ __launch_bounds__(256) void rmsnorm_hidden_kernel(NormArgs a) {
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int i = lane + 64 * c;
-    if (i < nc) {
-      uint16_t r[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint16_t xb = half_of(xr[c], e);
-        r[e] = a.res ? rne_bf16((double)bf_to_f(xb) + (double)bf_to_f(half_of(rr[c], e)))
-                     : xb;
-        const double rv = (double)bf_to_f(r[e]);
-        ss += rv * rv;
-      }
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) rr[c][e2] = (uint32_t)r[2 * e2] | ((uint32_t)r[2 * e2 + 1] << 16);
-    }
+    if (i < nc) rr[c] = add_piece(xr[c], rr[c], a.res != nullptr, ss);
   }
   ss = wave_sum(ss);
   const double s = sqrt(ss / (double)a.hidden + a.eps);
@@ -90,22 +116,38 @@ __global__ __launch_bounds__(256) void rmsnorm_hidden_kernel(NormArgs a) {
   for (int c = 0; c < CH; ++c) {
     const int i = lane + 64 * c;
     if (i < nc) {
-      u32x4 o;
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        uint16_t ob[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int e = 2 * e2 + h;
-          const uint16_t yb = rne_bf16((double)bf_to_f(half_of(rr[c], e)) / s);
-          ob[h] = a.w ? rne_bf16((double)bf_to_f(half_of(wr[c], e)) * (double)bf_to_f(yb))
-                      : yb;
-        }
-        o[e2] = (uint32_t)ob[0] | ((uint32_t)ob[1] << 16);
-      }
-      st16(a.out + row + 8 * i, o);
+      st16(a.out + row + 8 * i, norm_piece(rr[c], wr[c], a.w != nullptr, s));
       if (a.res) st16(a.res + row + 8 * i, rr[c]);
     }
+  }
+}
+
+// Up to kNormRowTokens rows: one workgroup per row and one 16-byte piece per
+// thread, so a row's serial fp64 work is one piece deep instead of hidden/512
+// pieces; the waves' sums of squares meet in LDS and are added in wave order.
+__global__ __launch_bounds__(1024) void rmsnorm_row_kernel(NormArgs a) {
+  __shared__ double s_ss[16];
+  const int i = threadIdx.x, w = i >> 6, nw = blockDim.x >> 6;
+  const int nc = a.hidden >> 3;
+  const size_t row = (size_t)blockIdx.x * a.hidden;
+  const bool on = i < nc;
+  u32x4 xr = {0u, 0u, 0u, 0u}, rr = xr, wr = xr;
+  if (on) {
+    xr = ld16(a.x + row + 8 * i);
+    if (a.res) rr = ld16(a.res + row + 8 * i);
+    if (a.w) wr = ld16(a.w + 8 * i);
+  }
+  double ss = 0.0;
+  if (on) rr = add_piece(xr, rr, a.res != nullptr, ss);
+  ss = wave_sum(ss);
+  if ((i & 63) == 0) s_ss[w] = ss;
+  __syncthreads();
+  double tot = 0.0;
+  for (int v = 0; v < nw; ++v) tot += s_ss[v];
+  const double s = sqrt(tot / (double)a.hidden + a.eps);
+  if (on) {
+    st16(a.out + row + 8 * i, norm_piece(rr, wr, a.w != nullptr, s));
+    if (a.res) st16(a.res + row + 8 * i, rr);
   }
 }
 
@@ -126,6 +168,13 @@ static hipError_t launch_ch(const NormArgs& a, hipStream_t s,
 
 hipError_t launch_rmsnorm_hidden(const NormArgs& a, hipStream_t s) {
   if (a.n_tokens == 0) return hipSuccess;
+  if (a.n_tokens <= kNormRowTokens) {
+    const int nc = a.hidden >> 3;
+    if (nc < 1 || nc > 1024) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(rmsnorm_row_kernel, dim3(a.n_tokens), dim3(64 * ((nc + 63) / 64)), 0, s,
+                       a);
+    return hipGetLastError();
+  }
   return launch_ch(a, s, std::make_integer_sequence<int, kNormMaxChunks>{});
 }
 

@@ -78,6 +78,18 @@ def test_decode_rows_and_ragged_tail():
     run_epilogue(300, 512, 2560, seed=52, weight=False, o_pad=64)
 
 
+def test_streaming_path_token_tiles():
+    """Up to 32 tokens run the streaming kernel: one and two token tiles of 16,
+    a ragged second tile, the largest batch it takes, and every width of K it
+    has a variant for; 33 tokens go back to the GEMM."""
+    run_epilogue(17, 4096, 2560, seed=56)
+    run_epilogue(32, 4096, 2560, seed=57, o_pad=128)
+    run_epilogue(16, 2048, 1024, seed=58, weight=False)
+    run_epilogue(3, 8192, 512, seed=59)
+    run_epilogue(5, 512, 256, seed=60)
+    run_epilogue(33, 4096, 2560, seed=61)
+
+
 def test_other_widths():
     run_epilogue(130, 1024, 4096, seed=53)
     run_epilogue(1, 64, 128, seed=54)

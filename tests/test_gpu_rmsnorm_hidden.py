@@ -49,8 +49,9 @@ def test_qwen3_4b_rows(residual, weight):
     run(2048, 2560, residual, weight, seed=60)
 
 
+# up to 512 rows run one workgroup per row, more run one wave per row
 @pytest.mark.parametrize("T,H", [(1, 8), (3, 128), (7, 520), (65, 4096),
-                                 (5, 8192)])
+                                 (5, 8192), (512, 2560), (513, 2560), (600, 8192)])
 def test_shapes(T, H):
     run(T, H, True, True, seed=61)
 
