@@ -132,7 +132,7 @@ constexpr float kOutLimit = 0x1p126f;
 struct WaveAttn {
   f32x16 o[4];  // O^T, d-block db: rows d = 32*db + 8*(r/4) + 4*h2 + r%4
   float m;      // reference max (log2 domain), per query
-  float lsum;   // sum of this lane's half of the bf16-rounded probabilities
+  float lsum;   // sum of this lane's half of the probabilities (fp32, before rounding)
   uint32_t kb;  // LDS byte offset of this lane's K operand at k-step 0
   uint32_t vb;  // LDS byte offset of this lane's V^T piece at d-block 0
 
@@ -239,24 +239,29 @@ struct WaveAttn {
     return fmaxf(mt, __shfl_xor(mt, 32));
   }
 
-  // Scores -> bf16 P^T (pb[c]: keys 16c .. 16c+15) with the reference max;
-  // the row sum accumulates the rounded values.
+  // Scores -> bf16 P^T (pb[c]: keys 16c .. 16c+15) with the reference max.
+  // The row sum adds the fp32 probabilities before their rounding to bf16
+  // (a pairwise tree per tile, plain fp32 adds).  A v_dot2 over the packed
+  // values gives the same sum within the rounding, but it does not overlap
+  // MFMAs on the same SIMD (an MFMA wave and a dot2 wave sharing one take
+  // the sum of their times), while fp32 adds do.
   template <bool MASK>
   __device__ __forceinline__ void probs(f32x16& s0, f32x16& s1, int kv0, int lim_abs,
                                         int h2, u32x4 (&pb)[4]) {
     if (MASK) mask(s0, s1, kv0, lim_abs, h2);
+    float part[8];
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      pb[r >> 3][(r & 7) >> 1] = pack_bf16x2(__builtin_amdgcn_exp2f(s0[r] - m),
-                                             __builtin_amdgcn_exp2f(s0[r + 1] - m));
-      pb[2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(__builtin_amdgcn_exp2f(s1[r] - m),
-                                                   __builtin_amdgcn_exp2f(s1[r + 1] - m));
+      const float e0 = __builtin_amdgcn_exp2f(s0[r] - m);
+      const float e1 = __builtin_amdgcn_exp2f(s0[r + 1] - m);
+      const float e2 = __builtin_amdgcn_exp2f(s1[r] - m);
+      const float e3 = __builtin_amdgcn_exp2f(s1[r + 1] - m);
+      pb[r >> 3][(r & 7) >> 1] = pack_bf16x2(e0, e1);
+      pb[2 + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(e2, e3);
+      part[r >> 1] = (e0 + e1) + (e2 + e3);
     }
-    constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 (1, 1)
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) lsum = dot2_bf16(pb[c][i], kOnes, lsum);
+    lsum += ((part[0] + part[1]) + (part[2] + part[3])) +
+            ((part[4] + part[5]) + (part[6] + part[7]));
   }
 
   // QK of the next tile (K tile kn, into sn) interleaved with the
@@ -269,12 +274,12 @@ struct WaveAttn {
                                            int h2, u32x4 (&pb)[4]) {
     qk(kn, kbt, qb, sn0, sn1);
     probs<MASK>(sc0, sc1, kv0, lim_abs, h2, pb);
-    // 16 MFMAs, 16 LDS reads and ~100 VALU: one MFMA, one read, six VALU
+    // 16 MFMAs, 16 LDS reads and ~110 VALU: one MFMA, one read, seven VALU
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
     }
   }
 
