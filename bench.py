@@ -397,6 +397,38 @@ def rmsnorm_rate(torch, qa, reps=20):
             "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
 
 
+def epilogue_rate(torch, qa):
+    """qa_attn_epilogue (output projection 4096 -> 2560 with the residual add,
+    then the post-attention RMSNorm) at the workload's two shapes: the
+    prefill layer's 4 x 2048 tokens, and one decode step's 4 tokens with w_o
+    rotated over 16 copies (336 MB, past the 256 MB MALL) as a model's layers
+    would be.  Graph-timed replays; flops 2 T 4096 2560, and for the decode
+    shape the bytes of w_o per call."""
+    H, D = 2560, 4096
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    res = {}
+    for name, T, ncopy in (("prefill_tokens_8192", 8192, 1), ("decode_tokens_4", 4, 16)):
+        o = torch.randn(T, D, generator=g, device="cuda").to(torch.bfloat16)
+        ws = [(0.02 * torch.randn(H, D, generator=g, device="cuda")).to(torch.bfloat16)
+              for _ in range(ncopy)]
+        resid = torch.randn(T, H, generator=g, device="cuda").to(torch.bfloat16)
+        nw = torch.ones(H, device="cuda", dtype=torch.bfloat16)
+        out = torch.empty_like(resid)
+        n = max(4, ncopy)
+
+        def fn():
+            for i in range(n):
+                qa.attn_epilogue(o, ws[i % ncopy], resid, nw, 1e-6, out=out)
+        us, _ = _graph_time_us(torch, fn)
+        us /= n
+        fl = 2.0 * T * D * H
+        res[name] = {"us": round(us, 2), "TFLOPs": round(fl / (us * 1e-6) / 1e12, 1),
+                     "w_o_GBps": round(H * D * 2 / (us * 1e-6) / 1e9, 1)}
+        del ws
+    return res
+
+
 def _graph_time_us(torch, fn, reps=10, warm=2):
     """Median time of one replay of a graph that captures fn(), with events
     on the replaying stream (replays back to back, so no host enqueue gap
@@ -587,7 +619,8 @@ def profile_kernels(wl, torch, qa):
     """One pass of each hot kernel plus a copy of known size, for rocprofv3
     kernel-trace and counter runs: copy 256 MiB x3 (counter calibration),
     prefill of layer 0, one decode step over the 36 layers at context
-    2048 + 65, one verify call."""
+    2048 + 65, one verify call, and the attention epilogue at 8192 tokens
+    (GEMM) and at 4 tokens (streaming kernel)."""
     n = 256 << 20
     src = torch.empty(n, dtype=torch.uint8, device="cuda")
     dst = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -598,6 +631,11 @@ def profile_kernels(wl, torch, qa):
     for l in range(wl.L):
         wl.decode_layer(l)
     wl.verify()
+    for T in (8192, 4):
+        o = torch.randn(T, 4096, device="cuda").to(torch.bfloat16)
+        w_o = (0.02 * torch.randn(2560, 4096, device="cuda")).to(torch.bfloat16)
+        resid = torch.randn(T, 2560, device="cuda").to(torch.bfloat16)
+        qa.attn_epilogue(o, w_o, resid, None, 1e-6)
     torch.cuda.synchronize()
     ctx = wl.S + wl.steps // 2 + 1
     print(json.dumps({
@@ -739,7 +777,7 @@ def main():
         "prefill_TFLOPs": round(pre_tflops, 1),
         "prefill_frac_mfma_peak": round(pre_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "verify_us": round(ver_us, 2),
-        "roofline": {"kernel": "qa_decode call = decode_kernel<4,9> "
+        "roofline": {"kernel": "qa_decode call = decode_kernel<4,3> "
                                "(one launch, merge inside)", "bound": "hbm",
                      "achieved": round(dec_ach, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s",
@@ -763,8 +801,9 @@ def main():
     if not args.no_ragged:
         log("bench: ragged-batch latency spread (untimed)")
         result["ragged_spread"] = ragged_spread(torch, qa, W)
-        log("bench: hidden-state RMSNorm (untimed)")
+        log("bench: hidden-state RMSNorm, attention epilogue (untimed)")
         result["rmsnorm_hidden"] = rmsnorm_rate(torch, qa)
+        result["attn_epilogue"] = epilogue_rate(torch, qa)
         log("bench: membw probe, rotated verify, small workloads, chunked prefill")
         probe = membw_probe(torch, qa)
         probe["decode_frac_of_probe"] = round(dec_ach / probe["GBps"], 4)

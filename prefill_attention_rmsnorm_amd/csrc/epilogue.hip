@@ -47,7 +47,14 @@ __global__ __launch_bounds__(256) void epilogue_gemm_kernel(EpilogueArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char sA[2][kEpBM * 128];
   __shared__ __attribute__((aligned(16))) unsigned char sB[2][kEpBN * 128];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int n0 = blockIdx.x * kEpBN, m0 = blockIdx.y * kEpBM;
+  // Workgroups are dealt to the 8 XCDs round-robin by id: XCD x takes the
+  // token tiles x, x + 8, ... with the feature tiles varying fastest, so the
+  // n_nt workgroups that read one token tile of o share one L2.  Ids past the
+  // last token tile (the grid is rounded up to 8 of them) exit.
+  const int n_nt = a.hidden / kEpBN;
+  const int xcd = blockIdx.x & 7, li = blockIdx.x >> 3;
+  const int m0 = (xcd + 8 * (li / n_nt)) * kEpBM, n0 = (li % n_nt) * kEpBN;
+  if (m0 >= a.n_tokens) return;  // (workgroup-uniform, before any barrier)
   const int wm = (w >> 1) * 64, wn = (w & 1) * 64;
 
   // 16-byte chunks tid + 256 j (j < 4) of each 128 x 64 stage: row id >> 3,
@@ -194,7 +201,8 @@ hipError_t launch_attn_epilogue(const EpilogueArgs& a, const NormArgs& n, hipStr
       default: hipLaunchKernelGGL(epilogue_small_kernel<32>, grid, dim3(512), 0, s, a); break;
     }
   } else {
-    const dim3 grid(a.hidden / kEpBN, (a.n_tokens + kEpBM - 1) / kEpBM);
+    const int n_mt = (a.n_tokens + kEpBM - 1) / kEpBM;
+    const dim3 grid((unsigned)((a.hidden / kEpBN) * 8 * ((n_mt + 7) / 8)));
     hipLaunchKernelGGL(epilogue_gemm_kernel, grid, dim3(256), 0, s, a);
   }
   hipError_t e = hipGetLastError();
