@@ -55,12 +55,30 @@ def _compile(src: str) -> str:
     return obj
 
 
-def _sha(files) -> str:
+def _code_lines(text: str):
+    """The lines of a source with // comments and blank lines removed, so that
+    the hash below changes with the code only."""
+    for line in text.splitlines():
+        code = line.split("//", 1)[0].rstrip()
+        if code:
+            yield code
+
+
+def _sha(files, read=None) -> str:
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        if read is None:
+            with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+                text = fh.read()
+        else:
+            text = read(f)
+        for line in _code_lines(text):
+            h.update(line.encode() + b"\n")
     return h.hexdigest()[:16]
+
+
+DECODE_SOURCES = ["decode.hip", "merge.hip", "qa_device.h", "qa_internal.h",
+                  "merge_count.h", "merge_inline.h"]
 
 
 def _git(*args) -> str:
@@ -81,8 +99,7 @@ def _write_build_info():
                       "include"),
         "hipcc": ver[0] if ver else "",
         "arch": ARCH,
-        "decode_source_sha": _sha(["decode.hip", "merge.hip", "qa_device.h",
-                                   "qa_internal.h", "merge_count.h", "merge_inline.h"]),
+        "decode_source_sha": _sha(DECODE_SOURCES),
         "prefill_source_sha": _sha(["prefill.hip", "attn_tile.h",
                                     "qa_device.h", "qa_internal.h"]),
         "verify_source_sha": _sha(["verify.hip", "attn_tile.h", "qa_device.h",

@@ -1,21 +1,21 @@
 // Single-token decode on gfx950: split-K over the cache, memory-bound.
 //
 // "dryft-flash-infer" agent guide, Where the wins are: per-step overhead and
-// the preallocated, strided cache.  A workgroup owns (split, kv head,
-// sequence); the cache rows before the new position are cut into near-equal
-// runs, one per split, and each of the four waves owns the 16-key tiles
-// w, w+4, ... of its run.  A workgroup first loads the small inputs (the
-// position, the q rows, and for split 0 the new token's k/v row) and waits
-// for them, so q' is formed while the cache bytes stream in rather than
-// after them; then it issues every cache load of its run at once (K straight
-// into the B-operand layout of the 16x16x32 bf16 MFMA, V as whole rows).
-// Each wave scores its own tiles (heads x keys), takes its own max, turns
-// its scores into weights and forms P.V with dot2 instructions over the V
-// rows as loaded, exchanging the weights through a per-wave LDS patch only;
-// the four waves' (max, sum, output) are combined once, after one barrier.
-// The new token's K prologue (fp64, one RNE), its cache write and its key
-// are folded into split 0: one wave runs the prologue while the cache loads
-// are in flight and adds the new key to its own softmax.
+// the preallocated, strided cache.  A workgroup of eight waves owns (split,
+// kv head, sequence); the cache rows before the new position are cut into
+// near-equal runs, one per split, and wave w owns the 16-key tiles w, w+8,
+// ... of its run.  Every wave loads the small inputs (the position, the raw q
+// rows of all heads of the group) and forms q' for all heads itself, so no
+// wave waits for another before its first tile; its cache loads (K straight
+// into the B-operand layout of the 16x16x32 bf16 MFMA, V as whole rows) run
+// two tiles ahead of the tile it scores.  Each wave keeps an online softmax
+// per head (running max and sum, wave-uniform, the output rescaled when the
+// max grows), turns a tile's scores into weights, passes them through a
+// per-wave LDS patch to the P.V layout and forms P.V with dot2 instructions
+// over the V rows as loaded; the eight waves' (max, sum, output) are
+// combined once, after one barrier.  The new token is folded into split 0:
+// its last wave runs the fp64 K prologue (one RNE) and writes the slot before
+// issuing its own cache loads, and adds the new key to its softmax at the end.
 //
 // When the pairs fill whole rounds of the 8-XCD deal (a.sync set), the
 // partials are merged inside the launch.  Workgroups are dealt to the XCDs
