@@ -467,6 +467,163 @@ __device__ __forceinline__ float exact_row_max(const WaveAttn& st, const TileLoa
   return mx;
 }
 
+// ---- four-stage K/V ring ----------------------------------------------------
+//
+// For a run of a few tiles that streams from HBM, most copies of the run can
+// be in flight before the first tile is used.  Tile t's K sits in LDS buffer
+// t & 3 and its V likewise.  The copies go out in the order K0 V0 K1 V1 K2 V2
+// (ring_first: six tiles, which with a wave's few other loads stays within
+// the 63 memory operations its counter can track, so issue does not stall)
+// and then, at step j, K(j+3) and V(j+3), each into the buffer its previous
+// tile (K(j-1), V(j-1)) left by step j-1; copies of tiles past the run read
+// as zeros and are issued all the same, so at the top of step j exactly three
+// tiles' copies were issued after the ones it needs (K(j+1), V(j)), and
+// before the first step five after K0.  The waits count this wave's own
+// copies; the barrier after them makes every wave's pieces visible and ends
+// every read of the buffers about to be refilled.
+struct RingLds {
+  unsigned char *k0, *k1, *k2, *k3, *v0, *v1, *v2, *v3;
+};
+// The buffers by compile-time index, so that the compiler sees which LDS
+// array each read and each copy touches (a copy in flight into one buffer
+// then does not hold up reads of another).
+template <int I>
+__device__ __forceinline__ unsigned char* ring_k(const RingLds& r) {
+  if constexpr (I == 0) return r.k0;
+  else if constexpr (I == 1) return r.k1;
+  else if constexpr (I == 2) return r.k2;
+  else return r.k3;
+}
+template <int I>
+__device__ __forceinline__ unsigned char* ring_v(const RingLds& r) {
+  if constexpr (I == 0) return r.v0;
+  else if constexpr (I == 1) return r.v1;
+  else if constexpr (I == 2) return r.v2;
+  else return r.v3;
+}
+
+// Wait until at most N of this wave's vector memory operations are in flight
+// (s_waitcnt: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left at their
+// maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// A workgroup barrier that orders LDS only: this wave's LDS accesses drain
+// (lgkmcnt) and the "memory" clobber keeps the compiler from moving LDS
+// accesses across it.  __syncthreads() would also wait for every copy into
+// LDS in flight, which the ring keeps in flight on purpose.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int NW>
+__device__ __forceinline__ void ring_first(const TileLoader<NW>& ld, const RingLds& r,
+                                           const uint16_t* kbase, const uint16_t* vbase,
+                                           int64_t sp, int kbeg, int kend) {
+  ld.load_k(kbase, sp, kbeg, kend, r.k0);
+  ld.load_v(vbase, sp, kbeg, kend, r.v0);
+  ld.load_k(kbase, sp, kbeg + kKeyTile, kend, r.k1);
+  ld.load_v(vbase, sp, kbeg + kKeyTile, kend, r.v1);
+  ld.load_k(kbase, sp, kbeg + 2 * kKeyTile, kend, r.k2);
+  ld.load_v(vbase, sp, kbeg + 2 * kKeyTile, kend, r.v2);
+}
+
+// Step j (J4 = j & 3) of the ring: the probabilities of tile j interleaved
+// with the QK product of tile j+1, then P.V of tile j.  Tile j is unmasked.
+template <int J4, int NW>
+__device__ __forceinline__ void ring_step(WaveAttn& st, const TileLoader<NW>& ld,
+                                          const RingLds& r, const uint16_t* kbase,
+                                          const uint16_t* vbase, int64_t sp, int kbeg,
+                                          int kend, int j, uint32_t kbt, uint32_t vbt,
+                                          const u32x4 (&qb)[8], f32x16& sc0, f32x16& sc1,
+                                          int h2) {
+  wait_vmcnt<3 * TileLoader<NW>::NI>();  // K(j+1), V(j)
+  lds_barrier();
+  ld.load_k(kbase, sp, kbeg + (j + 3) * kKeyTile, kend, ring_k<(J4 + 3) & 3>(r));
+  ld.load_v(vbase, sp, kbeg + (j + 3) * kKeyTile, kend, ring_v<(J4 + 3) & 3>(r));
+  f32x16 sn0, sn1;
+  u32x4 pb[4];
+  st.qk_probs<false>(ring_k<(J4 + 1) & 3>(r), kbt, qb, sn0, sn1, sc0, sc1, 0, 0, h2, pb);
+  st.pv(ring_v<J4>(r), vbt, pb);
+  sc0 = sn0;
+  sc1 = sn1;
+}
+
+// One pass over keys kbeg .. kend-1 with the ring (the caller issued
+// ring_first).  Every tile but the last lies wholly below kend and at or
+// below every query's position (no mask); the last is masked when
+// last_masked.  With SET_M the reference max is taken from tile 0.  Ends
+// with every copy landed and a full barrier.
+template <bool SET_M, int NW>
+__device__ __forceinline__ void attend_ring_pass(WaveAttn& st, const TileLoader<NW>& ld,
+                                                 const RingLds& r, const uint16_t* kbase,
+                                                 const uint16_t* vbase, int64_t sp,
+                                                 int kbeg, int kend, bool last_masked,
+                                                 const u32x4 (&qb)[8], int lim_abs, int h2) {
+  const int n_kt = (kend - kbeg + kKeyTile - 1) / kKeyTile;
+  uint32_t kbt, vbt;
+  st.offsets(kbt, vbt);
+  wait_vmcnt<5 * TileLoader<NW>::NI>();  // K0
+  lds_barrier();
+  f32x16 sc0, sc1;
+  WaveAttn::qk(r.k0, kbt, qb, sc0, sc1);
+  if (SET_M) {
+    f32x16 t0 = sc0, t1 = sc1;
+    if (n_kt == 1 && last_masked) WaveAttn::mask(t0, t1, kbeg, lim_abs, h2);
+    st.m = WaveAttn::row_max(t0, t1);
+  }
+  int j = 0;
+  for (; j + 4 <= n_kt - 1; j += 4) {
+    ring_step<0>(st, ld, r, kbase, vbase, sp, kbeg, kend, j, kbt, vbt, qb, sc0, sc1, h2);
+    ring_step<1>(st, ld, r, kbase, vbase, sp, kbeg, kend, j + 1, kbt, vbt, qb, sc0, sc1, h2);
+    ring_step<2>(st, ld, r, kbase, vbase, sp, kbeg, kend, j + 2, kbt, vbt, qb, sc0, sc1, h2);
+    ring_step<3>(st, ld, r, kbase, vbase, sp, kbeg, kend, j + 3, kbt, vbt, qb, sc0, sc1, h2);
+  }
+  if (j < n_kt - 1) {
+    ring_step<0>(st, ld, r, kbase, vbase, sp, kbeg, kend, j, kbt, vbt, qb, sc0, sc1, h2);
+    ++j;
+    if (j < n_kt - 1) {
+      ring_step<1>(st, ld, r, kbase, vbase, sp, kbeg, kend, j, kbt, vbt, qb, sc0, sc1, h2);
+      ++j;
+      if (j < n_kt - 1) {
+        ring_step<2>(st, ld, r, kbase, vbase, sp, kbeg, kend, j, kbt, vbt, qb, sc0, sc1, h2);
+        ++j;
+      }
+    }
+  }
+  // the last tile: nothing left to load ahead, so every copy is waited for
+  wait_tile_loads();
+  __syncthreads();
+  u32x4 pb[4];
+  if (last_masked) st.probs<true>(sc0, sc1, kbeg + j * kKeyTile, lim_abs, h2, pb);
+  else st.probs<false>(sc0, sc1, kbeg + j * kKeyTile, lim_abs, h2, pb);
+  const unsigned char* vl = (j & 3) == 0 ? r.v0 : (j & 3) == 1 ? r.v1 : (j & 3) == 2 ? r.v2 : r.v3;
+  st.pv(vl, vbt, pb);
+  __syncthreads();
+}
+
+// attend_ring_pass with the exact-max fallback (the double-buffered pass over
+// the ring's first two K and V buffers).  The caller issued ring_first().
+template <int NW>
+__device__ __forceinline__ void attend_ring(WaveAttn& st, const TileLoader<NW>& ld,
+                                            const RingLds& r, const uint16_t* kbase,
+                                            const uint16_t* vbase, int64_t sp, int kbeg,
+                                            int kend, bool last_masked, const u32x4 (&qb)[8],
+                                            int lim_abs, int h2) {
+  attend_ring_pass<true>(st, ld, r, kbase, vbase, sp, kbeg, kend, last_masked, qb, lim_abs, h2);
+  if (__syncthreads_or(st.overflowed())) {
+    const AttnLds lds{r.k0, r.k1, r.v0, r.v1};
+    const int n_unmasked = (kend - kbeg) / kKeyTile;
+    st.m = exact_row_max(st, ld, lds, kbase, sp, kbeg, kend, qb, lim_abs, h2);
+    st.reset();
+    load_first(ld, lds, kbase, vbase, sp, kbeg, kend);
+    attend_pass<false>(st, ld, lds, kbase, vbase, sp, kbeg, kend, n_unmasked, qb, lim_abs, h2);
+  }
+}
+
 // Attention of this wave's 32 query rows over keys kbeg .. kend-1 (see
 // attend_pass), with the exact-max fallback.  The caller issued load_first().
 template <int NW>

@@ -19,6 +19,7 @@
 #include "attn_tile.h"
 #include "merge_inline.h"
 #include "qa.h"
+#include "verify_layout.h"
 
 namespace qa {
 
@@ -29,21 +30,35 @@ __device__ __forceinline__ uint32_t cs_lds_offset(int t, int i) {
   return (uint32_t)(t * 512 + (((i >> 1) ^ (t & 31)) << 4) + ((i & 1) << 3));
 }
 
-template <int G, int NW>
+// RING: the old-slot splits stream their tiles through the four-stage ring
+// of attn_tile.h (2 or 4 waves, blocks of up to kVerifyRingTokens tokens);
+// the block's own split, one tile long, takes the double-buffered pass over
+// the ring's first buffers.
+template <int G, int NW, bool RING>
 __global__ __launch_bounds__(NW * 64) void verify_kernel(DecodeArgs a, RopeFreq f) {
   constexpr int NT = NW * 64;
-  constexpr int kCsBytes = (128 / G) * 512;  // cos/sin rows of up to 128/G tokens
+  // cos/sin rows of the block's tokens: up to 128/G, or kVerifyRingTokens
+  constexpr int kCsBytes = (RING ? kVerifyRingTokens : 128 / G) * 512;
+  constexpr int kRingBytes = RING ? kKTileBytes : 16;
   __shared__ __attribute__((aligned(16))) unsigned char lds_k0[kKTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned char lds_k1[kKTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned char lds_v0[kKTileBytes];
-  // V tile 1 and the queries' cos/sin rows share one array: the rows are
-  // read by the query prologue, which every wave finishes before the first
-  // barrier of attend(), and V tile 1 is first copied in after that barrier.
-  // (For G >= 4 the rows fit in the tile, and two workgroups fit per CU.)
+  // Without the ring, V tile 1 and the queries' cos/sin rows share one
+  // array: the rows are read by the query prologue, which every wave
+  // finishes before the first barrier of attend(), and V tile 1 is first
+  // copied in after that barrier.  With it, the rows have their own array,
+  // since the ring's copies start before the prologue.
   __shared__ __attribute__((aligned(16)))
-  unsigned char lds_v1[kCsBytes > kKTileBytes ? kCsBytes : kKTileBytes];
+  unsigned char lds_v1[!RING && kCsBytes > kKTileBytes ? kCsBytes : kKTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_k2[kRingBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_k3[kRingBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_v2[kRingBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_v3[kRingBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_csr[RING ? kCsBytes : 16];
+  (void)lds_csr;
   const AttnLds lds{lds_k0, lds_k1, lds_v0, lds_v1};
-  unsigned char* lds_cs = lds_v1;
+  const RingLds ring{lds_k0, lds_k1, lds_k2, lds_k3, lds_v0, lds_v1, lds_v2, lds_v3};
+  unsigned char* lds_cs = RING ? lds_csr : lds_v1;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int j = l & 31, h2 = l >> 5;
@@ -119,98 +134,123 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(DecodeArgs a, RopeFreq 
     const uint16_t* vbase = a.c.v + (size_t)b * a.c.sb + (size_t)g * a.c.sh;
     TileLoader<NW> ld;
     ld.init(__builtin_amdgcn_readfirstlane(w), l, a.c.sp);
-
-    // ---- new slots: k' (fp64) and v into the cache.  Wave w takes slots
-    // L0 + w, L0 + w + NW, ...; the rotation advances from one slot to the
-    // next by the fp64 angle-addition identity (one turn by NW positions)
-    // instead of a fresh sincos per slot.
-    if (new_split && w < n) {  // (wave-uniform)
-      double cn, sn, cstep, sstep;
-      sincos((double)(L0 + w) * invf, &sn, &cn);
-      sincos((double)NW * invf, &sstep, &cstep);
-      for (int i0 = w; i0 < n; i0 += NW * CH) {
-        if (i0 != w) {  // later rounds (blocks longer than NW * CH)
-#pragma unroll
-          for (int c = 0; c < CH; ++c) {
-            const int i = min(i0 + NW * c, n - 1);
-            const size_t src = (((size_t)b * n + i) * a.n_kv_heads + g) * kHeadDim;
-            kx0[c] = a.k[src + l];
-            kx1[c] = a.k[src + l + 64];
-            vx[c] = reinterpret_cast<const uint32_t*>(a.v + src)[l];
-          }
-        }
-        // The slots' sums of squares are reduced across the wave together,
-        // one butterfly step for all of them at a time, so their shuffle
-        // latencies overlap.  Per slot the arithmetic is kprime_pair's: the
-        // same products and sums in the same order.
-        double ss[CH];
-        {
-#pragma clang fp contract(off)
-#pragma unroll
-          for (int c = 0; c < CH; ++c) {
-            const double x0 = (double)bf_to_f(kx0[c]), x1 = (double)bf_to_f(kx1[c]);
-            ss[c] = x0 * x0 + x1 * x1;
-          }
-#pragma unroll
-          for (int o = 32; o >= 1; o >>= 1)
-#pragma unroll
-            for (int c = 0; c < CH; ++c) ss[c] += __shfl_xor(ss[c], o);
-        }
-#pragma unroll
-        for (int c = 0; c < CH; ++c) {
-          const int i = i0 + NW * c;
-          if (i >= n) break;  // (wave-uniform)
-          uint16_t o0, o1;
-          {
-#pragma clang fp contract(off)
-            const double x0 = (double)bf_to_f(kx0[c]), x1 = (double)bf_to_f(kx1[c]);
-            const double rr = sqrt(ss[c] / 128.0 + a.eps);
-            const double y0 = x0 / rr * wk0;
-            const double y1 = x1 / rr * wk1;
-            o0 = f64_to_bf16_rne(y0 * cn - y1 * sn);
-            o1 = f64_to_bf16_rne(y1 * cn + y0 * sn);
-          }
-          const size_t crow =
-              (size_t)b * a.c.sb + (size_t)g * a.c.sh + (size_t)(L0 + i) * a.c.sp;
-          a.c.k[crow + l] = o0;
-          a.c.k[crow + l + 64] = o1;
-          reinterpret_cast<uint32_t*>(a.c.v + crow)[l] = vx[c];
-          const double c2 = cn * cstep - sn * sstep;
-          sn = sn * cstep + cn * sstep;
-          cn = c2;
-        }
-      }
-    }
-
+    // the queries' rotation frequency (the cos/sin loop below gives thread
+    // tid pair tid % 64 every time), loaded ahead of the ring's copies: the
+    // memory counter is in order, so a load behind them would wait for them
+    const double invf_cs = f.inv_freq[tid & (kHalf - 1)];
+    WaveAttn st;
+    st.init(l);
+    u32x4 qb[8];
+    const int lim_abs = row_ok ? min(p, k1 - 1) : k1 - 1;
     // ---- cos/sin of the draft positions for the queries (LDS), one entry
     // per thread at a time: the angle reduced to whole turns in fp64, then
     // the hardware's turn-based cos/sin (the queries are rounded to bf16
-    // for the MFMA, so fp32 suffices)
-    for (int e = tid; e < n * kHalf; e += NT) {
-      const int i = e >> 6, pi = e & (kHalf - 1);
-      const double turns = (double)(L0 + i) * f.inv_freq[pi] * 0.15915494309189535;
-      const float fr = (float)(turns - floor(turns));
-      *reinterpret_cast<float2*>(lds_cs + cs_lds_offset(i, pi)) =
-          make_float2(__builtin_amdgcn_cosf(fr), __builtin_amdgcn_sinf(fr));
+    // for the MFMA, so fp32 suffices); then q'.  With copies into LDS in
+    // flight the barrier orders LDS only, so that they stay in flight.
+    static_assert(NT % kHalf == 0, "thread tid takes pair tid % 64");
+    auto q_prologue = [&](bool copies_in_flight) {
+      for (int e = tid; e < n * kHalf; e += NT) {
+        const int i = e >> 6, pi = e & (kHalf - 1);
+        const double turns = (double)(L0 + i) * invf_cs * 0.15915494309189535;
+        const float fr = (float)(turns - floor(turns));
+        *reinterpret_cast<float2*>(lds_cs + cs_lds_offset(i, pi)) =
+            make_float2(__builtin_amdgcn_cosf(fr), __builtin_amdgcn_sinf(fr));
+      }
+      if (copies_in_flight) lds_barrier();
+      else __syncthreads();
+      qp.cs_from_lds(lds_cs, ti, h2);
+      qp.compute((float)a.eps, a.qscale, qb);
+    };
+    // An old-slot split with the ring runs straight through: its copies go
+    // out first, then the queries' prologue, then the tiles.  (Kept apart
+    // from the other path, so that the compiler's waits for the loads before
+    // the copies count the copies exactly instead of draining them.)
+    bool done = false;
+    if constexpr (RING) {
+      if (!new_split) {
+        ring_first(ld, ring, kbase, vbase, a.c.sp, k0, k1);
+        q_prologue(true);
+        // keys below k1 <= L0 <= every query's position: only a partial last
+        // tile is masked
+        attend_ring(st, ld, ring, kbase, vbase, a.c.sp, k0, k1,
+                    ((k1 - k0) & (kKeyTile - 1)) != 0, qb, lim_abs, h2);
+        done = true;
+      }
     }
-    __syncthreads();
-    u32x4 qb[8];
-    qp.cs_from_lds(lds_cs, ti, h2);
-    qp.compute((float)a.eps, a.qscale, qb);
-    // cache slots written by earlier calls: their first tiles load now, with
-    // q' already formed, so nothing but the copies stands before the first
-    // tile; the new slots' workgroup first orders its own cache writes
-    if (!new_split) load_first(ld, lds, kbase, vbase, a.c.sp, k0, k1);
-    __syncthreads();
-    if (new_split) load_first(ld, lds, kbase, vbase, a.c.sp, k0, k1);
-
-    WaveAttn st;
-    st.init(l);
-    const int lim_abs = row_ok ? min(p, k1 - 1) : k1 - 1;
-    // tiles whose keys all lie below k1 and at or below the first draft
-    // position need no mask
-    const int n_unmasked = max(min(k1 - 1, L0) + 1 - k0, 0) / kKeyTile;
-    attend(st, ld, lds, kbase, vbase, a.c.sp, k0, k1, n_unmasked, qb, lim_abs, h2);
+    if (!done) {
+      // ---- new slots: k' (fp64) and v into the cache.  Wave w takes slots
+      // L0 + w, L0 + w + NW, ...; the rotation advances from one slot to the
+      // next by the fp64 angle-addition identity (one turn by NW positions)
+      // instead of a fresh sincos per slot.
+      if (new_split && w < n) {  // (wave-uniform)
+        double cn, sn, cstep, sstep;
+        sincos((double)(L0 + w) * invf, &sn, &cn);
+        sincos((double)NW * invf, &sstep, &cstep);
+        for (int i0 = w; i0 < n; i0 += NW * CH) {
+          if (i0 != w) {  // later rounds (blocks longer than NW * CH)
+  #pragma unroll
+            for (int c = 0; c < CH; ++c) {
+              const int i = min(i0 + NW * c, n - 1);
+              const size_t src = (((size_t)b * n + i) * a.n_kv_heads + g) * kHeadDim;
+              kx0[c] = a.k[src + l];
+              kx1[c] = a.k[src + l + 64];
+              vx[c] = reinterpret_cast<const uint32_t*>(a.v + src)[l];
+            }
+          }
+          // The slots' sums of squares are reduced across the wave together,
+          // one butterfly step for all of them at a time, so their shuffle
+          // latencies overlap.  Per slot the arithmetic is kprime_pair's: the
+          // same products and sums in the same order.
+          double ss[CH];
+          {
+  #pragma clang fp contract(off)
+  #pragma unroll
+            for (int c = 0; c < CH; ++c) {
+              const double x0 = (double)bf_to_f(kx0[c]), x1 = (double)bf_to_f(kx1[c]);
+              ss[c] = x0 * x0 + x1 * x1;
+            }
+  #pragma unroll
+            for (int o = 32; o >= 1; o >>= 1)
+  #pragma unroll
+              for (int c = 0; c < CH; ++c) ss[c] += __shfl_xor(ss[c], o);
+          }
+  #pragma unroll
+          for (int c = 0; c < CH; ++c) {
+            const int i = i0 + NW * c;
+            if (i >= n) break;  // (wave-uniform)
+            uint16_t o0, o1;
+            {
+  #pragma clang fp contract(off)
+              const double x0 = (double)bf_to_f(kx0[c]), x1 = (double)bf_to_f(kx1[c]);
+              const double rr = sqrt(ss[c] / 128.0 + a.eps);
+              const double y0 = x0 / rr * wk0;
+              const double y1 = x1 / rr * wk1;
+              o0 = f64_to_bf16_rne(y0 * cn - y1 * sn);
+              o1 = f64_to_bf16_rne(y1 * cn + y0 * sn);
+            }
+            const size_t crow =
+                (size_t)b * a.c.sb + (size_t)g * a.c.sh + (size_t)(L0 + i) * a.c.sp;
+            a.c.k[crow + l] = o0;
+            a.c.k[crow + l + 64] = o1;
+            reinterpret_cast<uint32_t*>(a.c.v + crow)[l] = vx[c];
+            const double c2 = cn * cstep - sn * sstep;
+            sn = sn * cstep + cn * sstep;
+            cn = c2;
+          }
+        }
+      }
+      q_prologue(false);
+      // cache slots written by earlier calls: their first tiles load now,
+      // with q' already formed, so nothing but the copies stands before the
+      // first tile; the new slots' workgroup first orders its own cache writes
+      if (!new_split) load_first(ld, lds, kbase, vbase, a.c.sp, k0, k1);
+      __syncthreads();
+      if (new_split) load_first(ld, lds, kbase, vbase, a.c.sp, k0, k1);
+      // tiles whose keys all lie below k1 and at or below the first draft
+      // position need no mask
+      const int n_unmasked = max(min(k1 - 1, L0) + 1 - k0, 0) / kKeyTile;
+      attend(st, ld, lds, kbase, vbase, a.c.sp, k0, k1, n_unmasked, qb, lim_abs, h2);
+    }
     if (row_ok) {
       const float lt = st.lsum + __shfl_xor(st.lsum, 32);
       if (h2 == 0) {
@@ -241,12 +281,17 @@ static hipError_t launch_verify_g(const DecodeArgs& a, const RopeFreq& f,
                                   hipStream_t s) {
   const dim3 grid(a.n_split * a.n_kv_heads * a.batch);
   const int rows = a.block_len * G;
+  const bool ring = verify_uses_ring(G, a.block_len);
   if (rows <= 32)
-    hipLaunchKernelGGL((verify_kernel<G, 1>), grid, dim3(64), 0, s, a, f);
+    hipLaunchKernelGGL((verify_kernel<G, 1, false>), grid, dim3(64), 0, s, a, f);
+  else if (rows <= 64 && ring)
+    hipLaunchKernelGGL((verify_kernel<G, 2, true>), grid, dim3(128), 0, s, a, f);
   else if (rows <= 64)
-    hipLaunchKernelGGL((verify_kernel<G, 2>), grid, dim3(128), 0, s, a, f);
+    hipLaunchKernelGGL((verify_kernel<G, 2, false>), grid, dim3(128), 0, s, a, f);
+  else if (rows <= 128 && ring)
+    hipLaunchKernelGGL((verify_kernel<G, 4, true>), grid, dim3(256), 0, s, a, f);
   else if (rows <= 128)
-    hipLaunchKernelGGL((verify_kernel<G, 4>), grid, dim3(256), 0, s, a, f);
+    hipLaunchKernelGGL((verify_kernel<G, 4, false>), grid, dim3(256), 0, s, a, f);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

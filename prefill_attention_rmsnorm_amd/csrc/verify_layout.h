@@ -17,9 +17,18 @@ namespace qa {
 // a function of the launch sizes only.
 inline int verify_waves(int rows) { return rows <= 32 ? 1 : rows <= 64 ? 2 : 4; }
 
+// Blocks of up to this many tokens on 2 or 4 waves stream their old slots
+// through the four-stage K/V ring (eight 16 KB tiles and the cos/sin rows:
+// 144 KB of LDS, one workgroup per CU).  One wave would need 6 x 16 copies in
+// flight, more than its memory counter holds.
+constexpr int kVerifyRingTokens = 32;
+inline bool verify_uses_ring(int G, int block_len) {
+  return verify_waves(block_len * G) >= 2 && block_len <= kVerifyRingTokens;
+}
+
 inline int verify_workgroups_per_cu(int G, int block_len) {
   const int by_simd = 4 / verify_waves(block_len * G);
-  const int by_lds = G >= 4 ? 2 : 1;
+  const int by_lds = verify_uses_ring(G, block_len) ? 1 : G >= 4 ? 2 : 1;
   return by_simd < by_lds ? by_simd : by_lds;
 }
 
