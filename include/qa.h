@@ -60,7 +60,9 @@ typedef enum {
   QA_ERR_ALIGN = -4,       /* pointer or stride misaligned */
   QA_ERR_CAPACITY = -5,    /* context longer than the cache */
   QA_ERR_WORKSPACE = -6,   /* workspace missing or too small */
-  QA_ERR_HIP = -7          /* a HIP runtime call failed */
+  QA_ERR_HIP = -7,         /* a HIP runtime call failed */
+  QA_ERR_DEVICE = -8       /* debug mode only: a kernel of this call set a
+                              QA_DEVERR_* bit in the workspace error word */
 } qa_status;
 
 /* Operation codes for qa_workspace_bytes. */
@@ -306,6 +308,19 @@ void qa_reset_counters(void);
  * captured graph.
  */
 qa_status qa_device_error(void* ws, void* stream, int32_t* code);
+
+/*
+ * Debug mode, for bringing up a caller (fail-closed checking: pegainfer PR
+ * #862, review thread).  When on, every call that launches kernels then
+ * synchronises its stream and returns QA_ERR_HIP if a HIP error is pending,
+ * or QA_ERR_DEVICE if its workspace error word (decode_noalloc: *dev_err)
+ * holds any QA_DEVERR_* bit; the word is left as it is.  Calls on a stream
+ * that is being captured into a graph skip the check.  Off by default; the
+ * environment variable QA_DEBUG=1 turns it on for the process (read at the
+ * first call), qa_set_debug(1) or (0) at any time.  Debug mode costs a host
+ * synchronisation per call.
+ */
+void qa_set_debug(int on);
 
 #ifdef __cplusplus
 }

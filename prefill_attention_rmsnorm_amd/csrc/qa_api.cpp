@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 
@@ -43,6 +44,43 @@ qa_status hip_fail(hipError_t e, const char* what) {
   g_last_error = buf;
   g_counters[CNT_HIP_FAIL].fetch_add(1);
   return QA_ERR_HIP;
+}
+
+// Debug mode: -1 until first read from QA_DEBUG, then 0 or 1.
+std::atomic<int> g_debug{-1};
+
+bool debug_on() {
+  int d = g_debug.load(std::memory_order_relaxed);
+  if (d < 0) {
+    const char* env = std::getenv("QA_DEBUG");
+    int want = (env && env[0] && std::strcmp(env, "0") != 0) ? 1 : 0;
+    g_debug.compare_exchange_strong(d, want);  // a concurrent qa_set_debug wins
+    d = g_debug.load(std::memory_order_relaxed);
+  }
+  return d == 1;
+}
+
+// After a call's launches, in debug mode: wait for them and fail on a pending
+// HIP error or a set device error bit (err_word may be NULL).  A stream that
+// is being captured is not synchronised.
+qa_status debug_check(void* stream, const void* err_word, const char* what) {
+  if (!debug_on()) return QA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(s, &cap);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+  if (cap != hipStreamCaptureStatusNone) return QA_OK;
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, what);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, what);
+  if (err_word) {
+    int32_t v = 0;
+    e = hipMemcpy(&v, err_word, sizeof v, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "read error word");
+    if (v != 0) return fail(QA_ERR_DEVICE, "%s: device error bits 0x%x (debug mode)", what, v);
+  }
+  return QA_OK;
 }
 
 bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -271,6 +309,7 @@ qa_status qa_prefill(const qa_cache* c, const qa_params* p, const void* q,
   g_counters[CNT_KERNELS].fetch_add(nk);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   g_counters[CNT_PREFILL].fetch_add(1);
+  if (qa_status d = debug_check(stream, ws, "prefill"); d != QA_OK) return d;
   g_last_error.clear();
   return QA_OK;
 }
@@ -340,6 +379,7 @@ qa_status qa_decode(const qa_cache* c, const qa_params* p, const void* q,
   g_counters[CNT_KERNELS].fetch_add(nk);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   g_counters[CNT_DECODE].fetch_add(1);
+  if (qa_status d = debug_check(stream, ws, "decode"); d != QA_OK) return d;
   g_last_error.clear();
   return QA_OK;
 }
@@ -381,6 +421,7 @@ qa_status qa_decode_noalloc(const qa_cache* c, const qa_params* p, const void* q
   g_counters[CNT_KERNELS].fetch_add(nk);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   g_counters[CNT_DECODE].fetch_add(1);
+  if (qa_status d = debug_check(stream, dev_err, "decode_noalloc"); d != QA_OK) return d;
   g_last_error.clear();
   return QA_OK;
 }
@@ -419,6 +460,7 @@ qa_status qa_verify(const qa_cache* c, const qa_params* p, const void* q,
   g_counters[CNT_KERNELS].fetch_add(nk);
   if (e != hipSuccess) return hip_fail(e, "verify launch");
   g_counters[CNT_VERIFY].fetch_add(1);
+  if (qa_status d = debug_check(stream, ws, "verify"); d != QA_OK) return d;
   g_last_error.clear();
   return QA_OK;
 }
@@ -446,6 +488,7 @@ qa_status qa_rmsnorm_hidden(const void* x, void* residual, const void* weight,
   hipError_t e = qa::launch_rmsnorm_hidden(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");
   if (n_tokens > 0) g_counters[CNT_KERNELS].fetch_add(1);
+  if (qa_status d = debug_check(stream, nullptr, "rmsnorm_hidden"); d != QA_OK) return d;
   g_last_error.clear();
   return QA_OK;
 }
@@ -493,6 +536,7 @@ qa_status qa_attn_epilogue(const void* o, int64_t o_tok_stride, const void* w_o,
   hipError_t e = qa::launch_attn_epilogue(a, n, static_cast<hipStream_t>(stream), &nk);
   g_counters[CNT_KERNELS].fetch_add(nk);
   if (e != hipSuccess) return hip_fail(e, "epilogue launch");
+  if (qa_status d = debug_check(stream, nullptr, "attn_epilogue"); d != QA_OK) return d;
   g_last_error.clear();
   return QA_OK;
 }
@@ -505,7 +549,7 @@ qa_status qa_copy(const void* src, void* dst, size_t bytes, void* stream) {
   if (e != hipSuccess) return hip_fail(e, "copy launch");
   g_counters[CNT_COPY].fetch_add(1);
   g_counters[CNT_KERNELS].fetch_add(1);
-  return QA_OK;
+  return debug_check(stream, nullptr, "copy");
 }
 
 const char* qa_status_str(qa_status s) {
@@ -518,11 +562,14 @@ const char* qa_status_str(qa_status s) {
     case QA_ERR_CAPACITY: return "QA_ERR_CAPACITY";
     case QA_ERR_WORKSPACE: return "QA_ERR_WORKSPACE";
     case QA_ERR_HIP: return "QA_ERR_HIP";
+    case QA_ERR_DEVICE: return "QA_ERR_DEVICE";
   }
   return "QA_ERR_UNKNOWN";
 }
 
 const char* qa_last_error(void) { return g_last_error.c_str(); }
+
+void qa_set_debug(int on) { g_debug.store(on ? 1 : 0); }
 
 void qa_get_counters(uint64_t out[8]) {
   for (int i = 0; i < 8; ++i) out[i] = g_counters[i].load();

@@ -26,7 +26,7 @@ EXPORTS = (
     "qa_verify", "qa_copy",
     "qa_rmsnorm_hidden", "qa_attn_epilogue",
     "qa_status_str", "qa_last_error", "qa_get_counters", "qa_reset_counters",
-    "qa_device_error",
+    "qa_device_error", "qa_set_debug",
 )
 
 
@@ -95,6 +95,7 @@ def lib():
         "qa_get_counters": (None, [P(ctypes.c_uint64)]),
         "qa_reset_counters": (None, []),
         "qa_device_error": (_i32, [_vp, _vp, P(ctypes.c_int32)]),
+        "qa_set_debug": (None, [_i32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -405,6 +406,12 @@ def device_error(ws: torch.Tensor, stream=None) -> int:
     code = ctypes.c_int32(0)
     _check(lib().qa_device_error(_ptr(ws), _stream(stream), ctypes.byref(code)))
     return int(code.value)
+
+
+def set_debug(on: bool):
+    """qa_set_debug: synchronise and check every call (QA_ERR_DEVICE on a set
+    device error bit); also set by QA_DEBUG=1 in the environment."""
+    lib().qa_set_debug(1 if on else 0)
 
 
 def counters():

@@ -35,6 +35,7 @@ def test_status_strings():
     L = qa.lib()
     assert L.qa_status_str(0) == b"QA_OK"
     assert L.qa_status_str(-5) == b"QA_ERR_CAPACITY"
+    assert L.qa_status_str(-8) == b"QA_ERR_DEVICE"
 
 
 FAKE = 0x10000  # an aligned address that is never dereferenced
