@@ -165,10 +165,10 @@ struct DecodeArgs {
                    // NULL: merge kernel
 };
 
-// Attention epilogue GEMM: 128 x 128 output tiles, K in steps of 64.  Up to
+// Attention epilogue GEMM: 256 x 128 output tiles, K in steps of 64.  Up to
 // kEpSmallT tokens use the streaming kernel instead: kEpSmallN output features
 // per workgroup.
-constexpr int kEpBM = 128, kEpBN = 128, kEpBK = 64;
+constexpr int kEpBM = 256, kEpBN = 128, kEpBK = 64;
 constexpr int kEpSmallT = 32, kEpSmallN = 16;
 
 struct EpilogueArgs {
