@@ -510,7 +510,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int x, const 
 // Persistent grid, one workgroup per CU: each takes the next q-tile from a
 // counter in the workspace (zeroed by the K/V prologue of the same call)
 // until none is left, so the heaviest tiles start first and every CU stays
-// busy to the end instead of following the hardware's dispatch order.
+// busy to the end instead of following the hardware's dispatch order.  A
+// workgroup claims its next tile when it starts the current one.
 template <int G>
 __global__ __launch_bounds__(512, 1) void prefill_attn_kernel(PrefillArgs a) {
   constexpr int TQ = 256 / G;
@@ -523,17 +524,23 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_kernel(PrefillArgs a) {
   __shared__ int s_item;
   const AttnLds lds{lds_k0, lds_k1, lds_v0, lds_v1};
   const int n_items = a.n_seq * a.n_kv_heads * a.n_qtiles;
-  for (;;) {
+  if (threadIdx.x == 0)
+    s_item = __hip_atomic_fetch_add(a.tile_ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  int x = s_item;
+  while (x < n_items) {
+    // the next item is claimed as this one starts, so that the counter's
+    // round trip overlaps this item's work instead of following it; its
+    // number reaches the other waves through s_item after the item
+    int next = 0;
     if (threadIdx.x == 0)
-      s_item = __hip_atomic_fetch_add(a.tile_ctr, 1, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const int x = s_item;
-    __syncthreads();  // every wave has its item before s_item is rewritten
-    if (x >= n_items) break;
+      next = __hip_atomic_fetch_add(a.tile_ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     prefill_tile<G>(a, x, lds, lds_cs);
     wait_tile_loads();  // no copy into LDS outlives the tile
-    __syncthreads();    // nor any LDS read
+    __syncthreads();    // nor any LDS read; every wave has read s_item
+    if (threadIdx.x == 0) s_item = next;
+    __syncthreads();
+    x = s_item;
   }
 }
 
