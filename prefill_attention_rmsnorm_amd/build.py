@@ -45,9 +45,18 @@ def _flags():
     ]
 
 
+# Per-source extra flags.  prefill.hip: the prefill kernel claims its next
+# q-tile with a one-lane atomic in the middle of the current one and reads the
+# result only after it; the compiler's atomic optimizer would rewrite that
+# into a wave-wide atomic whose result it spreads over the lanes at once,
+# waiting for the round trip right there.
+EXTRA_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + _flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = ([hipcc()] + _flags() + EXTRA_FLAGS.get(src, [])
+           + ["-c", os.path.join(CSRC, src), "-o", obj])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n"

@@ -13,6 +13,12 @@
 
 namespace qa {
 
+// The XCDs a launch's workgroups are dealt over (round-robin by block index);
+// the attention grid keeps one q-tile counter per XCD in the workspace header
+// (ints 1..8, after the error word).
+constexpr int kPrefillXcds = 8;
+static_assert((1 + kPrefillXcds) * sizeof(int) <= kWsHeader, "counters fit the header");
+
 // One wave per token: cos/sin of its angles, then k' and v of every KV head.
 // Eight lanes per KV head and eight heads at a time: lane group gh (lanes
 // 8gh .. 8gh+7) holds head gh, lane sub = lane & 7 its rotation pairs
@@ -78,7 +84,7 @@ __device__ __forceinline__ void bf16x8_to_f64(u32x4 w, double (&d)[8]) {
 __global__ __launch_bounds__(256) void kv_prologue_kernel(PrefillArgs a,
                                                           RopeFreq f) {
   __shared__ double2 s_cs[4][kHalf];  // per wave: (cos, sin) of the 64 pairs
-  if (blockIdx.x == 0 && threadIdx.x == 0) *a.tile_ctr = 0;  // for the attention grid
+  if (blockIdx.x == 0 && threadIdx.x < kPrefillXcds) a.tile_ctr[threadIdx.x] = 0;  // for the attention grid
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wv;
   if (t >= a.total_tokens) return;
@@ -235,12 +241,34 @@ __device__ __forceinline__ void pp_mphase(WaveAttn& st, const AttnLds& lds, uint
   pin(st.o);
 }
 
+// The claim of a workgroup's next q-tile from the tile counter.  One lane
+// (kClaimThread, in group B) takes it kClaimLead key tiles before the end of
+// the current q-tile: late enough that the tile goes to whichever workgroup
+// frees up first (a claim at the start of a long q-tile would hold the next
+// one back behind it while other CUs idle), early enough that the counter's
+// round trip is hidden behind the last key tiles.
+constexpr int kClaimThread = 256, kClaimLead = 2;
+struct NextClaim {
+  int* ctr;
+  int at;     // key tile at which this wave claims; -1: none (wave-uniform)
+  int count;  // the count taken (lane kClaimThread), -1 before the claim;
+              // used only after the q-tile, so the atomic's return is not
+              // waited for in the middle of it
+  __device__ __forceinline__ void at_tile(int kk) {
+    if (kk == at) {
+      if (threadIdx.x == kClaimThread)
+        count = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      at = -1;
+    }
+  }
+};
+
 template <bool IS_B, bool SET_M>
 __device__ __forceinline__ void pingpong(WaveAttn& st, const TileLoader<4>& ld,
                                          const AttnLds& lds, const uint16_t* kbase,
                                          const uint16_t* vbase, int64_t sp, int kend,
                                          int n_kt, int n_unm, const u32x4 (&qb)[8],
-                                         int lim_abs, int h2) {
+                                         int lim_abs, int h2, NextClaim& nc) {
   uint32_t kbt, vbt;
   st.offsets(kbt, vbt);
   f32x16 s0, s1;
@@ -275,6 +303,7 @@ __device__ __forceinline__ void pingpong(WaveAttn& st, const TileLoader<4>& ld,
           pp_mphase<1>(st, lds, kbt, vbt, qb, pb, s0, s1, kk + 1 < n_kt);
         phase_barrier();
       } else {
+        nc.at_tile(kk);  // the atomic's return is waited for with the copies
         if (par == 0) pp_loads<1>(ld, lds, kbase, vbase, sp, kend, kk + 1, n_kt);
         else pp_loads<0>(ld, lds, kbase, vbase, sp, kend, kk + 1, n_kt);
         pp_vphase<SET_M>(st, s0, s1, kk, n_unm, lim_abs, h2, pb);  // phase 2kk+2
@@ -335,9 +364,9 @@ __device__ __forceinline__ void attend_pp(WaveAttn& st, const TileLoader<4>& ld,
                                           const AttnLds& lds, const uint16_t* kbase,
                                           const uint16_t* vbase, int64_t sp, int kend,
                                           int n_kt, int n_unm, const u32x4 (&qb)[8],
-                                          int lim_abs, int h2, bool is_b) {
-  if (is_b) pingpong<true, SET_M>(st, ld, lds, kbase, vbase, sp, kend, n_kt, n_unm, qb, lim_abs, h2);
-  else pingpong<false, SET_M>(st, ld, lds, kbase, vbase, sp, kend, n_kt, n_unm, qb, lim_abs, h2);
+                                          int lim_abs, int h2, bool is_b, NextClaim& nc) {
+  if (is_b) pingpong<true, SET_M>(st, ld, lds, kbase, vbase, sp, kend, n_kt, n_unm, qb, lim_abs, h2, nc);
+  else pingpong<false, SET_M>(st, ld, lds, kbase, vbase, sp, kend, n_kt, n_unm, qb, lim_abs, h2, nc);
 }
 
 // Work items are q-tiles, numbered heaviest first; when the number of
@@ -346,7 +375,7 @@ __device__ __forceinline__ void attend_pp(WaveAttn& st, const TileLoader<4>& ld,
 // (sequence, kv head), 256 query rows on 8 waves.
 template <int G>
 __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int x, const AttnLds& lds,
-                                             unsigned char* lds_cs) {
+                                             unsigned char* lds_cs, NextClaim& nc) {
   constexpr int TQ = 256 / G;            // tokens per workgroup
   constexpr int NPOS = (TQ + 63) / 64;   // positions per lane (each wave reads all)
   constexpr bool CS_LDS = G >= 4;
@@ -475,7 +504,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int x, const 
     qp.compute((float)a.eps, a.qscale, qb);
   }
   const bool is_b = w >= 4;
-  attend_pp<true>(st, ldb, lds, kbase, vbase, a.c.sp, kv_end, n_kt, n_unm, qb, p, h2, is_b);
+  if (w == kClaimThread / 64) nc.at = max(0, n_kt - kClaimLead);
+  attend_pp<true>(st, ldb, lds, kbase, vbase, a.c.sp, kv_end, n_kt, n_unm, qb, p, h2, is_b, nc);
   if (__syncthreads_or(st.overflowed())) {
     // a later score far above the first tile's max: redo with the exact one
     st.m = exact_row_max(st, ld, lds, kbase, a.c.sp, 0, kv_end, qb, p, h2);
@@ -484,7 +514,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int x, const 
     load_next_two(ld, lds, kbase, vbase, a.c.sp, kv_end);
     wait_first_tile();
     phase_barrier();
-    attend_pp<false>(st, ldb, lds, kbase, vbase, a.c.sp, kv_end, n_kt, n_unm, qb, p, h2, is_b);
+    attend_pp<false>(st, ldb, lds, kbase, vbase, a.c.sp, kv_end, n_kt, n_unm, qb, p, h2, is_b, nc);
   }
 
   const float lt = st.lsum + __shfl_xor(st.lsum, 32);
@@ -507,11 +537,16 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int x, const 
   }
 }
 
-// Persistent grid, one workgroup per CU: each takes the next q-tile from a
-// counter in the workspace (zeroed by the K/V prologue of the same call)
-// until none is left, so the heaviest tiles start first and every CU stays
-// busy to the end instead of following the hardware's dispatch order.  A
-// workgroup claims its next tile when it starts the current one.
+// Persistent grid, one workgroup per CU: workgroup b starts on q-tile b, and
+// after that takes the next q-tile of its XCD's share (tiles r, r + 8, ...
+// for XCD r = b mod 8, where the hardware deals block b) from that XCD's
+// counter in the workspace (zeroed by the K/V prologue of the same call), so
+// the heaviest tiles start first, every CU stays busy to the end, and the
+// tiles of one (sequence, kv head) pair stay with the L2 that holds its K and
+// V.  The next tile is claimed shortly before the current one ends
+// (NextClaim), or after it when it had no key tiles to attend; the first
+// tiles are not claimed at all, so a workgroup that starts early cannot take
+// a second tile while one that starts late finds none.
 template <int G>
 __global__ __launch_bounds__(512, 1) void prefill_attn_kernel(PrefillArgs a) {
   constexpr int TQ = 256 / G;
@@ -524,21 +559,22 @@ __global__ __launch_bounds__(512, 1) void prefill_attn_kernel(PrefillArgs a) {
   __shared__ int s_item;
   const AttnLds lds{lds_k0, lds_k1, lds_v0, lds_v1};
   const int n_items = a.n_seq * a.n_kv_heads * a.n_qtiles;
-  if (threadIdx.x == 0)
-    s_item = __hip_atomic_fetch_add(a.tile_ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  int x = s_item;
+  const int xcd = blockIdx.x % kPrefillXcds;
+  // the XCD's tiles taken by the first round (one per block of the XCD)
+  const int first = ((int)gridDim.x - xcd + kPrefillXcds - 1) / kPrefillXcds;
+  int* const ctr = a.tile_ctr + xcd;
+  int x = blockIdx.x;  // the grid is never wider than the item count
   while (x < n_items) {
-    // the next item is claimed as this one starts, so that the counter's
-    // round trip overlaps this item's work instead of following it; its
-    // number reaches the other waves through s_item after the item
-    int next = 0;
-    if (threadIdx.x == 0)
-      next = __hip_atomic_fetch_add(a.tile_ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    prefill_tile<G>(a, x, lds, lds_cs);
+    NextClaim nc{ctr, -1, -1};
+    prefill_tile<G>(a, x, lds, lds_cs, nc);
     wait_tile_loads();  // no copy into LDS outlives the tile
     __syncthreads();    // nor any LDS read; every wave has read s_item
-    if (threadIdx.x == 0) s_item = next;
+    if (threadIdx.x == kClaimThread) {
+      const int c = nc.count >= 0
+                        ? nc.count
+                        : __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_item = xcd + kPrefillXcds * (first + c);
+    }
     __syncthreads();
     x = s_item;
   }
@@ -562,7 +598,10 @@ hipError_t launch_prefill(const PrefillArgs& a0, const RopeFreq& f, int group,
     e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   const long n_items = (long)a.n_seq * a.n_kv_heads * a.n_qtiles;
-  const dim3 grid((unsigned)(n_items < n_cu ? n_items : n_cu));
+  // a wider item count gets a whole number of blocks per XCD, so that every
+  // XCD's share of the tiles has workgroups to take it
+  const long n_wg = n_items <= n_cu ? n_items : std::max(kPrefillXcds, n_cu / kPrefillXcds * kPrefillXcds);
+  const dim3 grid((unsigned)n_wg);
   switch (group) {
     case 1: hipLaunchKernelGGL(prefill_attn_kernel<1>, grid, dim3(512), 0, s, a); break;
     case 2: hipLaunchKernelGGL(prefill_attn_kernel<2>, grid, dim3(512), 0, s, a); break;

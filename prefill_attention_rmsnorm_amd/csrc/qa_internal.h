@@ -138,7 +138,7 @@ struct PrefillArgs {
   uint16_t* out;
   float* lse;
   int* err;
-  int* tile_ctr;  // q-tile counter of the attention grid (workspace header)
+  int* tile_ctr;  // per-XCD q-tile counters of the attention grid (workspace header)
   float2* cs;  // cos/sin table in the workspace, [total_tokens][64]
 };
 
