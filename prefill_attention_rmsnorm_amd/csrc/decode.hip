@@ -7,15 +7,18 @@
 // ... of its run.  Every wave loads the small inputs (the position, the raw q
 // rows of all heads of the group) and forms q' for all heads itself, so no
 // wave waits for another before its first tile; its cache loads (K straight
-// into the B-operand layout of the 16x16x32 bf16 MFMA, V as whole rows) run
-// two tiles ahead of the tile it scores.  Each wave keeps an online softmax
-// per head (running max and sum, wave-uniform, the output rescaled when the
-// max grows), turns a tile's scores into weights, passes them through a
-// per-wave LDS patch to the P.V layout and forms P.V with dot2 instructions
-// over the V rows as loaded; the eight waves' (max, sum, output) are
-// combined once, after one barrier.  The new token is folded into split 0:
-// its last wave runs the fp64 K prologue (one RNE) and writes the slot before
-// issuing its own cache loads, and adds the new key to its softmax at the end.
+// into the A-operand layout of the 16x16x32 bf16 MFMA, V as whole rows) run
+// two tiles ahead of the tile it scores.  Both products of a tile are MFMAs
+// with the heads on the column axis: the transposed scores S^T = K q'^T come
+// out in exactly the layout the P.V product takes its weights in (the keys
+// of the K operand are permuted to make it so), and O^T = V^T P^T takes V
+// from the rows as loaded, so a tile costs a few dozen vector instructions
+// and no LDS traffic.  Each wave keeps an online softmax per head (running
+// max and sum, the output rescaled when the max grows); the eight waves'
+// (max, sum, output) are combined once, after one barrier.  The new token is
+// folded into split 0: its last wave runs the fp64 K prologue (one RNE) and
+// writes the slot before issuing its own cache loads, and adds the new key to
+// its softmax at the end.
 //
 // When the pairs fill whole rounds of the 8-XCD deal (a.sync set), the
 // partials are merged inside the launch.  Workgroups are dealt to the XCDs
@@ -34,30 +37,6 @@
 #include "qa_device.h"
 
 namespace qa {
-
-// Sum over the four 16-lane rows of a wave of N values per lane (N a multiple
-// of 4).  On return lane l holds N/4 sums: entry j is the sum of input
-// 4j + 2*((l >> 4) & 1) + ((l >> 5) & 1).  A 32-lane swap pairs inputs 2j and
-// 2j+1 so that lanes 0-31 add the two halves of one and lanes 32-63 of the
-// other; a 16-lane swap does the same between neighbouring rows.
-template <int N>
-__device__ __forceinline__ void rows4_sum(const float (&v)[N], float (&r)[N / 4]) {
-  float h[N / 2];
-#pragma unroll
-  for (int j = 0; j < N / 2; ++j) {
-    const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[2 * j]),
-                                                    __float_as_uint(v[2 * j + 1]),
-                                                    false, false);
-    h[j] = __uint_as_float(t[0]) + __uint_as_float(t[1]);
-  }
-#pragma unroll
-  for (int j = 0; j < N / 4; ++j) {
-    const auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(h[2 * j]),
-                                                    __float_as_uint(h[2 * j + 1]),
-                                                    false, false);
-    r[j] = __uint_as_float(t[0]) + __uint_as_float(t[1]);
-  }
-}
 
 // The raw q rows of all G heads of the group (elements lane and lane+64 of
 // each), the norm weights and the rotation frequency of pair `lane`; every
@@ -126,10 +105,6 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Position of key k (0..15) of a tile in the per-wave weight patch: lane
-// (kg, c) of the P.V step reads keys kg, kg+4, kg+8, kg+12 as one float4.
-__device__ __forceinline__ int pslot(int k) { return (k & 3) * 4 + (k >> 2); }
-
 // TPW: 16-key tiles per wave (a run is at most 16 * kDecodeWaves * TPW
 // rows); wave w owns the tiles w, w + kDecodeWaves, ... of its run.
 template <int G, int TPW>
@@ -138,7 +113,6 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 2) void decode_kernel(DecodeArgs
   static_assert(TPW >= 1 && TPW <= 4, "tiles per wave");
   static_assert(G <= 8, "group");
   __shared__ __attribute__((aligned(16))) uint16_t s_q[NW][G][kHeadDim];
-  __shared__ __attribute__((aligned(16))) float s_p[NW][G][16];
   __shared__ __attribute__((aligned(16))) float s_red[NW][G][kHeadDim];
   __shared__ float s_m[NW][G], s_l[NW][G];
 
@@ -163,7 +137,6 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 2) void decode_kernel(DecodeArgs
   const float ninf = -__builtin_inff();
   const bool nt_wave = split == 0 && w == NW - 1;  // the new token's prologue and key
   const int kg = lane >> 4, c = lane & 15;
-  const int hrow = 4 * (lane >> 4);  // first head of this lane's score registers
   uint16_t (*sq)[kHeadDim] = s_q[w];  // this wave's q'
 
   // ---- 1. the small loads: the position (the cache loads wait for it),
@@ -173,7 +146,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 2) void decode_kernel(DecodeArgs
   QRaw<G> qr;
   qr.load(a, f, b, g, lane);
   uint16_t nk0 = 0, nk1 = 0, nw0 = 0, nw1 = 0;
-  u32x4 nv = {0u, 0u, 0u, 0u};
+  u32x4 nv[4] = {};  // dims 32 kg + 8 r .. +7 for r < 4 (the O^T layout)
   if (nt_wave) {
     const uint16_t* kr = a.k + (size_t)pair * kHeadDim;
     nk0 = kr[lane];
@@ -181,7 +154,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 2) void decode_kernel(DecodeArgs
     const uint16_t* kwp = a.k_norm_w ? a.k_norm_w : a.q;
     nw0 = kwp[lane];
     nw1 = kwp[lane + 64];
-    nv = ld16(a.v + (size_t)pair * kHeadDim + 8 * c);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) nv[r] = ld16(a.v + (size_t)pair * kHeadDim + 32 * kg + 8 * r);
   }
   const bool ok = pos >= 0 && pos < a.max_ctx;
   if (!ok && split == 0 && g == 0 && tid == 0) flag_error(a.err, QA_DEVERR_POSITION);
@@ -190,18 +164,22 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 2) void decode_kernel(DecodeArgs
   // Rows [0, pos) -- all before the new slot -- in ns near-equal runs; keys
   // past the run are clamped to its last row (read again, their scores
   // masked), so every wave issues a fixed number of loads.  K: tile t, lane l
-  // holds dims 32 ks + 8 (l/16) .. +7 of key 16 t + l%16 (the B operand of
-  // k-step ks).  V: lane (kg, c) holds dims 8c .. 8c+7 of keys 16 t + kg + 4u.
+  // holds dims 32 ks + 8 (l/16) .. +7 of key 16 t + kperm(l%16) (row l%16 of
+  // the A operand of k-step ks).  V: lane (kg, c) holds dims 8c .. 8c+7 of
+  // keys 16 t + kg + 4u, u < 4.
   const int nrows = ok ? pos : 0;
   const int k0 = (int)((long)split * nrows / ns);
   const int k1 = (int)((long)(split + 1) * nrows / ns);
   const int klast = max(k1 - 1, 0);
   const uint16_t* kbase = a.c.k + (size_t)b * a.c.sb + (size_t)g * a.c.sh;
   const uint16_t* vbase = a.c.v + (size_t)b * a.c.sb + (size_t)g * a.c.sh;
+  // A-operand row m holds key (m >> 2) + 4 (m & 3): score register r of lane
+  // (kb, n) is then key kb + 4 r, the key that lane's V rows hold
+  const int kperm = (c >> 2) + 4 * (c & 3);
   u32x4 kq[TPW][4], vr[TPW][4];
   auto issue = [&](int i) {
     const int t0 = k0 + 16 * (w + NW * i);
-    const uint16_t* kr = kbase + (size_t)min(t0 + (lane & 15), klast) * a.c.sp + 8 * kg;
+    const uint16_t* kr = kbase + (size_t)min(t0 + kperm, klast) * a.c.sp + 8 * kg;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) kq[i][ks] = ld16(kr + 32 * ks);
 #pragma unroll
@@ -224,7 +202,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 2) void decode_kernel(DecodeArgs
     const size_t crow = (size_t)b * a.c.sb + (size_t)g * a.c.sh + (size_t)pos * a.c.sp;
     a.c.k[crow + lane] = o0;
     a.c.k[crow + lane + 64] = o1;
-    if (kg == 0) st16(a.c.v + crow + 8 * c, nv);
+    if (c == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st16(a.c.v + crow + 32 * kg + 8 * r, nv[r]);
+    }
     kn0 = bf_to_f(o0);
     kn1 = bf_to_f(o1);
   }
@@ -247,7 +228,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 2) void decode_kernel(DecodeArgs
                 (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(snew[h]), 32)) +
                  __int_as_float(__builtin_amdgcn_readlane(__float_as_int(snew[h]), 48)));
   }
-  u32x4 qv[4];  // the A operand: q' of head l%16, dims 32 ks + 8 (l/16) .. +7
+  u32x4 qv[4];  // the B operand: q' of head l%16, dims 32 ks + 8 (l/16) .. +7
   {
     const int qh = min(lane & 15, G - 1);
     const bool qvalid = (lane & 15) < G;
@@ -258,122 +239,88 @@ __global__ __launch_bounds__(64 * kDecodeWaves, 2) void decode_kernel(DecodeArgs
     }
   }
 
-  // ---- 4. the wave's tiles in arrival order, online softmax: per head a
-  // running max m and sum l (wave-uniform), the output rescaled when m grows.
-  // Scores have the heads on the MFMA row axis (lane l: head 4 (l/16) + r of
-  // key l%16); the weights go through the wave's LDS patch to the P.V
-  // layout, where lane (kg, c) takes keys (kg, kg+8) and (kg+4, kg+12) of
-  // the tile as bf16 pairs for dot2.
-  float mrun[G], lrun[G];
+  // ---- 4. the wave's tiles in arrival order, online softmax per head.
+  // Lane (kb, n) = (l/16, l%16) holds head n's scores of keys kb + 4 r of the
+  // tile (S^T register r), which are also the B operand (P^T) of the
+  // 16x16x16 P.V product: its K index 4 kb + r is key kb + 4 r.  The A
+  // operand (V^T) of output dims 8 m + j, j < 8, takes from lane (kb, m) the
+  // bf16 j of its V rows kb + 4 r.  So lane (kb, n) accumulates dims
+  // 32 kb + 8 r + j of head n in acc[j][r].  Its running max and sum are
+  // head n's (equal in the four lanes of the head); lanes of heads n >= G see
+  // a zero q' and are never stored.
+  const int n_h = c;
+  float mrun = ninf, lrun = 0.f;
+  f32x4 acc[8];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    mrun[h] = ninf;
-    lrun[h] = 0.f;
-  }
-  float acc[G * 8];
-#pragma unroll
-  for (int n = 0; n < G * 8; ++n) acc[n] = 0.f;
+  for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
     const int t0 = k0 + 16 * (w + NW * i);
-    if (t0 < k1) {  // (wave-uniform)
+    if (t0 < k1) {  // (wave-uniform; key t0 is in the run)
       f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) sc = mfma16x16x32(qv[ks], kq[i][ks], sc);
-      const bool kok = t0 + (lane & 15) < k1;
-      float tm[4];
+      for (int ks = 0; ks < 4; ++ks) sc = mfma16x16x32(kq[i][ks], qv[ks], sc);
+      float tm = ninf;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        sc[r] = (kok && hrow + r < G) ? sc[r] : ninf;
-        tm[r] = row16_max(sc[r]);
+        sc[r] = t0 + kg + 4 * r < k1 ? sc[r] : ninf;
+        tm = fmaxf(tm, sc[r]);
       }
-      // the new running max and the factor for what was accumulated so far
-      // (key t0 is in the run, so every head's tile max is finite)
-      float mnew[G], alpha[G];
+      const float mnew = fmaxf(mrun, rows4_max(tm));
+      const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);  // 0 while mrun = -inf
+      float pr[4];
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float th = __int_as_float(
-            __builtin_amdgcn_readlane(__float_as_int(tm[h & 3]), 16 * (h >> 2)));
-        mnew[h] = fmaxf(mrun[h], th);
-        alpha[h] = mrun[h] == ninf ? 0.f : __builtin_amdgcn_exp2f(mrun[h] - mnew[h]);
+      for (int r = 0; r < 4; ++r) pr[r] = __builtin_amdgcn_exp2f(sc[r] - mnew);
+      lrun = lrun * alpha + rows4_add((pr[0] + pr[1]) + (pr[2] + pr[3]));
+      mrun = mnew;
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {  // (wave-uniform)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] *= alpha;
       }
-      float ps[4];
+      const u32x2 pb = {pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float mr = mnew[0];
-#pragma unroll
-        for (int h = 1; h < G; ++h) mr = hrow + r == h ? mnew[h] : mr;
-        const float pr = __builtin_amdgcn_exp2f(sc[r] - mr);
-        if (hrow + r < G) s_p[w][hrow + r][pslot(lane & 15)] = pr;
-        ps[r] = row16_sum(pr);
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float th = __int_as_float(
-            __builtin_amdgcn_readlane(__float_as_int(ps[h & 3]), 16 * (h >> 2)));
-        lrun[h] = lrun[h] * alpha[h] + th;
-        mrun[h] = mnew[h];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[8 * h + e] *= alpha[h];
-      }
-      wave_lds_sync();  // the weight patch
-      uint32_t pa[G], pb[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float4 pq = *reinterpret_cast<const float4*>(&s_p[w][h][4 * kg]);
-        pa[h] = pack_bf16x2(pq.x, pq.z);  // keys kg, kg+8
-        pb[h] = pack_bf16x2(pq.y, pq.w);  // keys kg+4, kg+12
-      }
-      wave_lds_sync();  // read before the next tile rewrites it
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const uint32_t v0 = vr[i][0][e2], v2 = vr[i][2][e2];
-        const uint32_t v1 = vr[i][1][e2], v3 = vr[i][3][e2];
-        const uint32_t lo02 = (v0 & 0xffffu) | (v2 << 16), hi02 = (v0 >> 16) | (v2 & 0xffff0000u);
-        const uint32_t lo13 = (v1 & 0xffffu) | (v3 << 16), hi13 = (v1 >> 16) | (v3 & 0xffff0000u);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          acc[8 * h + 2 * e2] = dot2_bf16(pa[h], lo02, acc[8 * h + 2 * e2]);
-          acc[8 * h + 2 * e2 + 1] = dot2_bf16(pa[h], hi02, acc[8 * h + 2 * e2 + 1]);
-          acc[8 * h + 2 * e2] = dot2_bf16(pb[h], lo13, acc[8 * h + 2 * e2]);
-          acc[8 * h + 2 * e2 + 1] = dot2_bf16(pb[h], hi13, acc[8 * h + 2 * e2 + 1]);
-        }
+      for (int j = 0; j < 8; ++j) {
+        const int e2 = j >> 1;
+        const uint32_t v0 = vr[i][0][e2], v1 = vr[i][1][e2];
+        const uint32_t v2 = vr[i][2][e2], v3 = vr[i][3][e2];
+        // bf16 j of rows (u, u+1): bytes 0-1 (j even) or 2-3 (j odd) of each
+        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        const u32x2 av = {__builtin_amdgcn_perm(v1, v0, sel), __builtin_amdgcn_perm(v3, v2, sel)};
+        acc[j] = mfma16x16x16(av, pb, acc[j]);
       }
     }
     if (i + 2 < TPW) issue(i + 2);
   }
   // the new key: one more step of the online softmax (its weight in fp32),
-  // its value added once (key group 0)
+  // its value added once
   if (nt_wave && ok) {
+    float sn = snew[0];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mnew = fmaxf(mrun[h], snew[h]);
-      const float alpha = mrun[h] == ninf ? 0.f : __builtin_amdgcn_exp2f(mrun[h] - mnew);
-      const float pn = __builtin_amdgcn_exp2f(snew[h] - mnew);
-      lrun[h] = lrun[h] * alpha + pn;
-      mrun[h] = mnew;
+    for (int h = 1; h < G; ++h) sn = n_h == h ? snew[h] : sn;
+    const float mnew = fmaxf(mrun, sn);
+    const float alpha = mrun == ninf ? 0.f : __builtin_amdgcn_exp2f(mrun - mnew);
+    const float pn = __builtin_amdgcn_exp2f(sn - mnew);
+    lrun = lrun * alpha + pn;
+    mrun = mnew;
 #pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        acc[8 * h + 2 * e2] = acc[8 * h + 2 * e2] * alpha + (kg == 0 ? pn * bf_lo(nv[e2]) : 0.f);
-        acc[8 * h + 2 * e2 + 1] =
-            acc[8 * h + 2 * e2 + 1] * alpha + (kg == 0 ? pn * bf_hi(nv[e2]) : 0.f);
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t vw = nv[r][j >> 1];
+        acc[j][r] = acc[j][r] * alpha + pn * ((j & 1) ? bf_hi(vw) : bf_lo(vw));
       }
-    }
   }
-  // the wave's four key groups, then its (max, sum, output) for the combine
-  {
-    float red[2 * G];
-    rows4_sum<G * 8>(acc, red);
-    const int s16 = (lane >> 4) & 1, s32 = (lane >> 5) & 1;
+  // the wave's (max, sum, output) for the combine
+  if (n_h < G) {
 #pragma unroll
-    for (int j = 0; j < 2 * G; ++j)
-      s_red[w][j >> 1][8 * c + 4 * (j & 1) + 2 * s16 + s32] = red[j];
-    if (lane == 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        s_m[w][h] = mrun[h];
-        s_l[w][h] = lrun[h];
-      }
+    for (int r = 0; r < 4; ++r) {
+      float* d = &s_red[w][n_h][32 * kg + 8 * r];
+      *reinterpret_cast<float4*>(d) = make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]);
+      *reinterpret_cast<float4*>(d + 4) = make_float4(acc[4][r], acc[5][r], acc[6][r], acc[7][r]);
+    }
+    if (kg == 0) {
+      s_m[w][n_h] = mrun;
+      s_l[w][n_h] = lrun;
     }
   }
   __syncthreads();

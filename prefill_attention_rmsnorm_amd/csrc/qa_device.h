@@ -73,7 +73,32 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
       __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// D(16x16 fp32) += A(16x16 bf16) * B(16x16 bf16).  Lane l holds
+// A[l%16][4*(l/16) .. +3] and B[4*(l/16) .. +3][l%16] as two bf16 pairs
+// each, and D rows 4*(l/16) + r of column l%16 for register r.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma16x16x16(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                   __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
 // ---- cross-lane ------------------------------------------------------------
+// Max / sum over the lanes l, l^16, l^32, l^48 (one lane of each 16-lane
+// row); every lane gets the result.  permlane32_swap(x, x) returns x and x of
+// the lane 32 away; permlane16_swap(x, x) the same for the lane 16 away.
+__device__ __forceinline__ float rows4_max(float x) {
+  auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+  t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float rows4_add(float x) {
+  auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(t[0]) + __uint_as_float(t[1]);
+  t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL,
