@@ -194,6 +194,17 @@ def test_full_size_ragged():
     say(f"FULLSIZE_STATS prefill_ragged {lens} {st}")
 
 
+@pytest.mark.parametrize("lens,Hq,Hkv,cap", [
+    ([2048, 512, 512, 512], 32, 8, 2176),  # one heavy sequence: most late q-tiles empty
+    ([2900, 700, 1900], 8, 2, 3008),       # 6 pairs (not a multiple of 8), 276 q-tiles
+])
+def test_skewed_batches_over_the_persistent_grid(lens, Hq, Hkv, cap):
+    # every row against the oracle where the workgroups take their further
+    # q-tiles from the per-XCD counters with a skewed mix of tile weights
+    _, _, st = run_prefill(lens, Hq, Hkv, cap, seed=16)
+    say(f"FULLSIZE_STATS prefill_skewed {lens} {st}")
+
+
 def test_chunked_prefill_full_size():
     # B=4 prompts of 2048 fed as four 512-token chunks per sequence, each
     # chunk attending to the slots the earlier chunks wrote; every row of
