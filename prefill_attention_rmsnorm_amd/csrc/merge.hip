@@ -26,11 +26,17 @@ __global__ __launch_bounds__(128) void merge_kernel(DecodeArgs a, int G) {
   const float* pm = a.part_m + r0;
   const float* pl = a.part_l + r0;
   const float* po = a.part_o + r0 * kHeadDim + d4;
-  const MergeOut mo = merge_splits<16>(a.n_split, [&](int s, float& m, float& l, float4& o) {
+  auto load = [&](int s, float& m, float& l, float4& o) {
     m = pm[(size_t)s * rows];
     l = pl[(size_t)s * rows];
     o = *reinterpret_cast<const float4*>(po + (size_t)s * rows * kHeadDim);
-  });
+  };
+  // loads in flight per batch: the split count rounded up to 4, 8 or 16, so
+  // that no batch carries more clamped duplicate loads than it must
+  const int ns = a.n_split;
+  const MergeOut mo = ns <= 4   ? merge_splits<4>(ns, load)
+                      : ns <= 8 ? merge_splits<8>(ns, load)
+                                : merge_splits<16>(ns, load);
   const int n = a.block_len;
   const int hl = rr / n, ti = rr % n;
   const size_t orow = (((size_t)b * n + ti) * a.n_q_heads + g * G + hl) * kHeadDim;
