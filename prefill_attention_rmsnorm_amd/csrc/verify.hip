@@ -262,9 +262,11 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(DecodeArgs a, RopeFreq 
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
-          float4 v4 = make_float4(st.o[db][4 * a4], st.o[db][4 * a4 + 1],
-                                  st.o[db][4 * a4 + 2], st.o[db][4 * a4 + 3]);
-          *reinterpret_cast<float4*>(po + 32 * db + 8 * a4 + 4 * h2) = v4;
+          // non-temporal: the partials are read once, by the merge kernel on
+          // whichever XCD, so they need not stay in this XCD's L2
+          const f32x4 v4 = {st.o[db][4 * a4], st.o[db][4 * a4 + 1], st.o[db][4 * a4 + 2],
+                            st.o[db][4 * a4 + 3]};
+          __builtin_nontemporal_store(v4, reinterpret_cast<f32x4*>(po + 32 * db + 8 * a4 + 4 * h2));
         }
     }
   } else {
