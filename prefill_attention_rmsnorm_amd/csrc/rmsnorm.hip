@@ -8,20 +8,25 @@
 // residual stream is a bf16 tensor, so:
 //   r   = bf16(x + residual)                 (r = x without a residual)
 //   out = bf16(w * bf16(r / sqrt(mean(r^2) + eps)))
-// with every other step exact.  The kernel computes in fp64: a sum of two
-// bf16 values is exact there, and so is the product of two bf16 values; the
-// sum of squares is reordered (it differs from another order by ~1e-16
-// relative).  Each rounding to bf16 is one round to nearest even of the fp64
-// value, and the division is a correctly rounded fp64 division.
+// with every other step exact.  Each rounding to bf16 is one round to
+// nearest even of the exact value:
+// - the sum of two bf16 values and the product of two bf16 values are exact
+//   in fp32 (at most 24 significant bits, all multiples of 2^-133), so they
+//   are formed in fp32 and rounded once;
+// - the sum of squares is accumulated in fp64 (reordered: it differs from
+//   another order by ~1e-16 relative);
+// - r / s is formed in fp32 as r * (1/s) and rounded from there unless it
+//   lies within a few fp32 ulps of a bf16 rounding midpoint (its error is at
+//   most ~3 2^-24 relative, under 2 ulps), where the correctly rounded fp64
+//   division decides; values that are not finite or near the subnormal range
+//   take the fp64 steps too.
 //
 // One wave per token row: all loads of the row first (CH 16-byte pieces per
 // lane, CH = ceil(hidden / 512), a template argument so that registers are
 // sized for the row at hand), the sum of squares reduced across the wave,
 // then the row written back.  Batches of at most kNormRowTokens rows spread
-// each row over a workgroup instead (rmsnorm_row_kernel).  The traffic is 2 bytes per element for each of
-// x, residual in, out and residual out; at the measured rate the per-element
-// fp64 arithmetic and roundings (a few dozen instructions), not the bytes,
-// set the time.
+// each row over a workgroup instead (rmsnorm_row_kernel).  The traffic is 2
+// bytes per element for each of x, residual in, out and residual out.
 #include <utility>
 
 #include "qa.h"
@@ -45,13 +50,27 @@ __device__ __forceinline__ uint16_t rne_bf16(double x) {
   return f64_to_bf16_rne(x);
 }
 
+// fp32 -> bf16 bits, round to nearest even, for a finite or infinite value.
+__device__ __forceinline__ uint16_t rne16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Whether the fp32 value f leaves the fast path: not finite, or below 2^-118
+// in magnitude (near the subnormal range, where fp32 products lose bits).
+__device__ __forceinline__ bool off_range(float f) {
+  const uint32_t e = (__float_as_uint(f) >> 23) & 0xFFu;
+  return e < 9u || e == 0xFFu;
+}
+
 __device__ __forceinline__ uint16_t half_of(const u32x4& v, int e) {
   const uint32_t w = v[e >> 1];
   return (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
 }
 
 // The 8 values of one 16-byte piece: r = bf16(x + residual) (r = x without
-// a residual), their squares added to ss.
+// a residual), formed in fp32 (exact for a finite sum; an overflowing sum or
+// a NaN takes the fp64 steps), their squares added to ss in fp64.
 __device__ __forceinline__ u32x4 add_piece(u32x4 x, u32x4 res, bool has_res, double& ss) {
   u32x4 out;
 #pragma unroll
@@ -60,8 +79,13 @@ __device__ __forceinline__ u32x4 add_piece(u32x4 x, u32x4 res, bool has_res, dou
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint16_t xb = half_of(x, 2 * e2 + h);
-      r[h] = has_res ? rne_bf16((double)bf_to_f(xb) + (double)bf_to_f(half_of(res, 2 * e2 + h)))
-                     : xb;
+      r[h] = xb;
+      if (has_res) {
+        const float xf = bf_to_f(xb), rf = bf_to_f(half_of(res, 2 * e2 + h));
+        const float sf = xf + rf;
+        r[h] = ((__float_as_uint(sf) >> 23) & 0xFFu) == 0xFFu ? rne_bf16((double)xf + (double)rf)
+                                                              : rne16(sf);
+      }
       const double rv = (double)bf_to_f(r[h]);
       ss += rv * rv;
     }
@@ -70,8 +94,13 @@ __device__ __forceinline__ u32x4 add_piece(u32x4 x, u32x4 res, bool has_res, dou
   return out;
 }
 
-// out = bf16(w * bf16(r / s)) (no weight: bf16(r / s)) for the 8 values of a piece.
-__device__ __forceinline__ u32x4 norm_piece(u32x4 r, u32x4 w, bool has_w, double s) {
+// out = bf16(w * bf16(r / s)) (no weight: bf16(r / s)) for the 8 values of a
+// piece, inv = 1/s rounded to fp32.  r / s is formed as r * inv and rounded
+// from there unless it lies within 8 fp32 ulps of a bf16 rounding midpoint
+// (its error is under 2 ulps) or outside the fast range, where the correctly
+// rounded fp64 division decides; w * bf16(r / s) is exact in fp32 in range.
+__device__ __forceinline__ u32x4 norm_piece(u32x4 r, u32x4 w, bool has_w, double s,
+                                            float inv) {
   u32x4 o;
 #pragma unroll
   for (int e2 = 0; e2 < 4; ++e2) {
@@ -79,16 +108,31 @@ __device__ __forceinline__ u32x4 norm_piece(u32x4 r, u32x4 w, bool has_w, double
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int e = 2 * e2 + h;
-      const uint16_t yb = rne_bf16((double)bf_to_f(half_of(r, e)) / s);
-      ob[h] = has_w ? rne_bf16((double)bf_to_f(half_of(w, e)) * (double)bf_to_f(yb)) : yb;
+      const float rv = bf_to_f(half_of(r, e));
+      const float q = rv * inv;
+      const uint32_t lo = __float_as_uint(q) & 0xFFFFu;
+      // (a zero quotient is exact, or rounds to zero in fp64 too)
+      const bool exact_div =
+          (off_range(q) && q != 0.f) || (lo > 0x8000u - 8u && lo < 0x8000u + 8u);
+      const uint16_t yb = exact_div ? rne_bf16((double)rv / s) : rne16(q);
+      ob[h] = yb;
+      if (has_w) {
+        const float wf = bf_to_f(half_of(w, e));
+        const float p = wf * bf_to_f(yb);
+        ob[h] = off_range(p) && p != 0.f ? rne_bf16((double)wf * (double)bf_to_f(yb))
+                                         : rne16(p);
+      }
     }
     o[e2] = (uint32_t)ob[0] | ((uint32_t)ob[1] << 16);
   }
   return o;
 }
 
+// The weights load after the residual add, once x and the residual are
+// dead; rows of up to 5 pieces per lane (hidden <= 2560) then fit six waves
+// per SIMD without spilling.
 template <int CH>
-__global__ __launch_bounds__(256) void rmsnorm_hidden_kernel(NormArgs a) {
+__global__ __launch_bounds__(256, CH <= 5 ? 6 : 1) void rmsnorm_hidden_kernel(NormArgs a) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= a.n_tokens) return;  // (wave-uniform)
@@ -101,7 +145,6 @@ __global__ __launch_bounds__(256) void rmsnorm_hidden_kernel(NormArgs a) {
     if (i < nc) {
       xr[c] = ld16(a.x + row + 8 * i);
       if (a.res) rr[c] = ld16(a.res + row + 8 * i);
-      if (a.w) wr[c] = ld16(a.w + 8 * i);
     }
   }
   double ss = 0.0;
@@ -110,13 +153,20 @@ __global__ __launch_bounds__(256) void rmsnorm_hidden_kernel(NormArgs a) {
     const int i = lane + 64 * c;
     if (i < nc) rr[c] = add_piece(xr[c], rr[c], a.res != nullptr, ss);
   }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int i = lane + 64 * c;
+    if (i < nc && a.w) wr[c] = ld16(a.w + 8 * i);
+  }
   ss = wave_sum(ss);
   const double s = sqrt(ss / (double)a.hidden + a.eps);
+  const float inv = (float)(1.0 / s);
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int i = lane + 64 * c;
     if (i < nc) {
-      st16(a.out + row + 8 * i, norm_piece(rr[c], wr[c], a.w != nullptr, s));
+      st16(a.out + row + 8 * i, norm_piece(rr[c], wr[c], a.w != nullptr, s, inv));
       if (a.res) st16(a.res + row + 8 * i, rr[c]);
     }
   }
@@ -146,7 +196,7 @@ __global__ __launch_bounds__(1024) void rmsnorm_row_kernel(NormArgs a) {
   for (int v = 0; v < nw; ++v) tot += s_ss[v];
   const double s = sqrt(tot / (double)a.hidden + a.eps);
   if (on) {
-    st16(a.out + row + 8 * i, norm_piece(rr, wr, a.w != nullptr, s));
+    st16(a.out + row + 8 * i, norm_piece(rr, wr, a.w != nullptr, s, (float)(1.0 / s)));
     if (a.res) st16(a.res + row + 8 * i, rr);
   }
 }
