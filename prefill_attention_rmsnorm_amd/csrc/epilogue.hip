@@ -24,13 +24,17 @@
 //
 // Decode-sized batches (at most kEpSmallT tokens) take a second kernel: the
 // GEMM grid would be a few tiles wide there, while the work is one streaming
-// read of w_o.  A workgroup owns kEpSmallN output features and its eight waves
+// read of w_o.  A workgroup owns nf <= kEpSmallN output features, nf chosen so
+// that the grid covers the CUs (10 for hidden 2560: 256 workgroups, where 16
+// would leave 96 CUs without a share of the stream), and its eight waves
 // split K into eighths; each lane holds its wave's slice of those weight rows
 // in registers (all loads in flight at once), token tiles of 16 run
 // v_mfma_f32_16x16x32_bf16 over them (tokens on the row axis, the 16
 // features on the column axis), and the eight
 // partial sums of an output are added in wave order through LDS, so the
 // result does not depend on timing.
+#include <algorithm>
+
 #include "attn_tile.h"
 #include "qa.h"
 #include "qa_device.h"
@@ -38,6 +42,9 @@
 #include "rmsnorm.h"
 
 namespace qa {
+
+// The streaming kernel's grid aims at this many workgroups (one per CU).
+constexpr int kEpSmallCUs = 256;
 
 // LDS byte offset of chunk c of row r in a stage (128-byte rows).
 __device__ __forceinline__ uint32_t ep_swz(int row, int chunk) {
@@ -201,25 +208,30 @@ __global__ __launch_bounds__(512) void epilogue_gemm_kernel(EpilogueArgs a) {
     }
 }
 
+// nf: output features per workgroup (1 .. kEpSmallN); MFMA columns from nf
+// on, and features past the hidden size in the last workgroup, repeat a
+// valid weight row and are never stored.
 template <int KS>
-__global__ __launch_bounds__(512) void epilogue_small_kernel(EpilogueArgs a) {
+__global__ __launch_bounds__(512) void epilogue_small_kernel(EpilogueArgs a, int nf) {
   static_assert(kEpSmallN == 16, "one feature per MFMA column");
   __shared__ float part[8][16][kEpSmallN + 1];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int n0 = blockIdx.x * kEpSmallN;
+  const int n0 = blockIdx.x * nf;
   const int kw = w * (32 * KS);  // this wave's K range: kw .. kw + 32 KS - 1
   const int kq = 8 * (l >> 4);   // the lane's 8 k values within a 32-wide step
   // B operand of step s: W[n0 + (l & 15)][kw + 32 s + kq .. +7]
   u32x4 wb[KS];
-  const uint16_t* wrow = a.w + (size_t)(n0 + (l & 15)) * a.in_dim + kw + kq;
+  const int wf = min(n0 + min(l & 15, nf - 1), a.hidden - 1);
+  const uint16_t* wrow = a.w + (size_t)wf * a.in_dim + kw + kq;
 #pragma unroll
   for (int s = 0; s < KS; ++s) wb[s] = ld16(wrow + 32 * s);
   // the residual element each of the first 256 threads adds to, read now so
   // that its latency overlaps the weight stream (the next tile's is read
   // after this tile's store)
-  const int tr = tid / kEpSmallN, f = tid % kEpSmallN;
-  uint16_t* rp = a.res + (size_t)min(tr, a.n_tokens - 1) * a.hidden + n0 + f;
-  uint16_t rv = tid < 16 * kEpSmallN ? *rp : (uint16_t)0;
+  const int tr = tid / nf, f = tid - tr * nf;
+  const bool fout = tid < 16 * nf && n0 + f < a.hidden;  // (token row, feature) of this thread
+  uint16_t* rp = a.res + (size_t)min(tr, a.n_tokens - 1) * a.hidden + min(n0 + f, a.hidden - 1);
+  uint16_t rv = fout ? *rp : (uint16_t)0;
   for (int t0 = 0; t0 < a.n_tokens; t0 += 16) {
     const int tt = min(t0 + (l & 15), a.n_tokens - 1);  // rows past the last repeat it
     const uint16_t* orow = a.o + (size_t)tt * a.o_stride + kw + kq;
@@ -236,7 +248,7 @@ __global__ __launch_bounds__(512) void epilogue_small_kernel(EpilogueArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) part[w][4 * (l >> 4) + r][l & 15] = acc[r];
     __syncthreads();
-    if (tid < 16 * kEpSmallN) {
+    if (fout) {
       const int tok = t0 + tr;
       float sum = part[0][tr][f];
 #pragma unroll
@@ -262,13 +274,14 @@ hipError_t launch_attn_epilogue(const EpilogueArgs& a, const NormArgs& n, hipStr
   const bool small = a.n_tokens <= kEpSmallT && a.in_dim % 256 == 0 &&
                      (ks == 2 || ks == 4 || ks == 8 || ks == 16 || ks == 32);
   if (small) {
-    const dim3 grid(a.hidden / kEpSmallN);
+    const int nf = std::min(kEpSmallN, std::max(1, (a.hidden + kEpSmallCUs - 1) / kEpSmallCUs));
+    const dim3 grid((a.hidden + nf - 1) / nf);
     switch (ks) {
-      case 2: hipLaunchKernelGGL(epilogue_small_kernel<2>, grid, dim3(512), 0, s, a); break;
-      case 4: hipLaunchKernelGGL(epilogue_small_kernel<4>, grid, dim3(512), 0, s, a); break;
-      case 8: hipLaunchKernelGGL(epilogue_small_kernel<8>, grid, dim3(512), 0, s, a); break;
-      case 16: hipLaunchKernelGGL(epilogue_small_kernel<16>, grid, dim3(512), 0, s, a); break;
-      default: hipLaunchKernelGGL(epilogue_small_kernel<32>, grid, dim3(512), 0, s, a); break;
+      case 2: hipLaunchKernelGGL(epilogue_small_kernel<2>, grid, dim3(512), 0, s, a, nf); break;
+      case 4: hipLaunchKernelGGL(epilogue_small_kernel<4>, grid, dim3(512), 0, s, a, nf); break;
+      case 8: hipLaunchKernelGGL(epilogue_small_kernel<8>, grid, dim3(512), 0, s, a, nf); break;
+      case 16: hipLaunchKernelGGL(epilogue_small_kernel<16>, grid, dim3(512), 0, s, a, nf); break;
+      default: hipLaunchKernelGGL(epilogue_small_kernel<32>, grid, dim3(512), 0, s, a, nf); break;
     }
   } else {
     const int n_mt = (a.n_tokens + kEpBM - 1) / kEpBM;

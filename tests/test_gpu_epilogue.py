@@ -90,6 +90,14 @@ def test_streaming_path_token_tiles():
     run_epilogue(33, 4096, 2560, seed=61)
 
 
+def test_streaming_path_feature_split():
+    """The streaming kernel's output features per workgroup follow the width:
+    11 for 2688 (245 workgroups, the last holding 4 features) and the cap of
+    16 for 4096."""
+    run_epilogue(4, 1024, 2688, seed=62)
+    run_epilogue(2, 512, 4096, seed=63, weight=False)
+
+
 def test_other_widths():
     run_epilogue(130, 1024, 4096, seed=53)
     run_epilogue(1, 64, 128, seed=54)
