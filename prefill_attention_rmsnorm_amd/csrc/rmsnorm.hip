@@ -10,13 +10,15 @@
 //   out = bf16(w * bf16(r / sqrt(mean(r^2) + eps)))
 // with every other step exact.  Each rounding to bf16 is one round to
 // nearest even of the exact value:
-// - the sum of two bf16 values and the product of two bf16 values are exact
-//   in fp32 (at most 24 significant bits, all multiples of 2^-133), so they
-//   are formed in fp32 and rounded once;
+// - the sum of two bf16 values is formed in fp32: it is exact there unless
+//   the smaller term is below 2^-15 of the larger, and then too small to
+//   move the bf16 rounding, so rounding the fp32 sum once gives the bf16 of
+//   the exact sum; the product of two bf16 values (16 significant bits) is
+//   exact in fp32 in the normal range;
 // - the sum of squares is accumulated in fp64 (reordered: it differs from
 //   another order by ~1e-16 relative);
 // - r / s is formed in fp32 as r * (1/s) and rounded from there unless it
-//   lies within a few fp32 ulps of a bf16 rounding midpoint (its error is at
+//   lies within 8 fp32 ulps of a bf16 rounding midpoint (its error is at
 //   most ~3 2^-24 relative, under 2 ulps), where the correctly rounded fp64
 //   division decides; values that are not finite or near the subnormal range
 //   take the fp64 steps too.
@@ -173,7 +175,7 @@ __global__ __launch_bounds__(256, CH <= 5 ? 6 : 1) void rmsnorm_hidden_kernel(No
 }
 
 // Up to kNormRowTokens rows: one workgroup per row and one 16-byte piece per
-// thread, so a row's serial fp64 work is one piece deep instead of hidden/512
+// thread, so a row's serial work is one piece deep instead of hidden/512
 // pieces; the waves' sums of squares meet in LDS and are added in wave order.
 __global__ __launch_bounds__(1024) void rmsnorm_row_kernel(NormArgs a) {
   __shared__ double s_ss[16];
