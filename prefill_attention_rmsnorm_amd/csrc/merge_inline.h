@@ -1,5 +1,5 @@
-// Split-K partials merged inside the launch that wrote them (decode and
-// verify), through one XCD's L2.
+// Split-K partials merged inside the launch that wrote them (decode),
+// through one XCD's L2.
 //
 // Workgroups are dealt to the XCDs round-robin by id, so a grid numbered to
 // give all of a (sequence, kv head) pair's workgroups one id residue mod 8

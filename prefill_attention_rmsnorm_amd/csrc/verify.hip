@@ -17,7 +17,6 @@
 // that workgroup ever reads the block's slots in this call, and the block
 // barrier orders its own writes before its reads.
 #include "attn_tile.h"
-#include "merge_inline.h"
 #include "qa.h"
 #include "verify_layout.h"
 
@@ -62,19 +61,8 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(DecodeArgs a, RopeFreq 
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int j = l & 31, h2 = l >> 5;
-  // One-dimensional grid.  With the in-launch merge, id
-  // 8 * (split * npair / 8 + k) + x is split `split` of pair x + 8k, so a
-  // pair's workgroups share id mod 8 (one XCD); otherwise pairs are contiguous.
-  const int npair = a.batch * a.n_kv_heads, bid = blockIdx.x;
-  int pair, split;
-  if (a.sync) {
-    const int ppx = npair >> 3, idx = bid >> 3;
-    split = idx / ppx;
-    pair = (bid & 7) + 8 * (idx - split * ppx);
-  } else {
-    pair = bid / a.n_split;
-    split = bid - pair * a.n_split;
-  }
+  // One-dimensional grid, a pair's splits contiguous.
+  const int pair = blockIdx.x / a.n_split, split = blockIdx.x - pair * a.n_split;
   const int b = pair / a.n_kv_heads, g = pair - b * a.n_kv_heads;
   const int n = a.block_len;
   const int rows = n * G;
@@ -275,7 +263,6 @@ __global__ __launch_bounds__(NW * 64) void verify_kernel(DecodeArgs a, RopeFreq 
       a.part_l[rowbase + rr] = 0.f;
     }
   }
-  if (a.sync) merge_pair<NT, 4>(a, pair, b, g, G);
 }
 
 template <int G>
@@ -302,8 +289,7 @@ static hipError_t launch_verify_g(const DecodeArgs& a, const RopeFreq& f,
 hipError_t launch_verify(const DecodeArgs& a, const RopeFreq& f, int group,
                          hipStream_t s, int* n_kernels) {
   *n_kernels = 0;
-  if (a.sync && ((a.batch * a.n_kv_heads) % 8 != 0 || a.n_split > kInlineMaxSplits))
-    return hipErrorInvalidValue;  // the grid numbering and the counter fields
+  if (a.sync) return hipErrorInvalidValue;  // verify partials merge in their own launch
   hipError_t e;
   switch (group) {
     case 1: e = launch_verify_g<1>(a, f, s); break;
@@ -314,7 +300,6 @@ hipError_t launch_verify(const DecodeArgs& a, const RopeFreq& f, int group,
   }
   if (e != hipSuccess) return e;
   *n_kernels = 1;
-  if (a.sync) return hipSuccess;  // merged inside the launch
   e = launch_merge(a, group, s);
   if (e == hipSuccess) *n_kernels = 2;
   return e;
