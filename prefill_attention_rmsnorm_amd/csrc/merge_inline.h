@@ -7,8 +7,10 @@
 // workgroup stores its partial, waits for the stores and counts itself in on
 // the pair's counter with a device-scope atomic; the last one checks from the
 // counter that the pair really shared an XCD, drops its L1, reads the
-// partials from L2, merges them in split order (merge_splits_n, the
-// arithmetic of merge.hip) and returns the counter to zero.
+// partials from L2, merges them in split order (merge_splits_n in batches of
+// 8 splits; merge.hip takes the same single batch up to 8 splits, so the two
+// paths agree bit for bit there, and one batch of 16 above that) and returns
+// the counter to zero.
 #pragma once
 
 #include "qa.h"
