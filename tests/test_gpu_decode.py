@@ -109,6 +109,12 @@ def test_groups_and_short_contexts(Hq, Hkv):
     run_steps(3, Hq, Hkv, 200, [0, 1, 130], 3, seed=24)
 
 
+def test_merge_kernel_many_splits():
+    # 2 (sequence, kv head) pairs do not fill a round of the 8-XCD deal, so the
+    # partials go through the merge kernel: ~63 splits, several batches of 16
+    run_steps(1, 16, 2, 1100, [1000], 2, seed=28)
+
+
 def test_norm_weights():
     run_steps(2, 8, 2, 300, [100, 257], 2, seed=25, weights=True)
 

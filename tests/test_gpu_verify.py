@@ -58,6 +58,12 @@ def test_shapes(Hq, Hkv, n):
     run_verify(2, Hq, Hkv, 300, [100, 7], n, seed=42)
 
 
+def test_one_sequence_many_splits():
+    # 8 (sequence, kv head) pairs: 31 old-slot splits plus the block's own,
+    # merged by the merge kernel in two batches of 16 splits
+    run_verify(1, 32, 8, 2064, [2048], 16, seed=44)
+
+
 def test_large_batch_one_old_split():
     # 32 sequences x 8 kv heads: 256 pairs, one old-slot split per pair (plus
     # the block's own workgroup); starts from 0 (no old slots) upward
