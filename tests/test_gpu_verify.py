@@ -52,8 +52,10 @@ def test_ragged_starts_and_split_boundaries():
     run_verify(4, 32, 8, 1200, [0, 63, 500, 1180], 16, seed=41)
 
 
+# (8, 8, 48) and (16, 8, 40): blocks past 32 tokens take the double-buffered
+# pass without the ring, on 2 waves (48 rows) and on 4 waves (80 rows)
 @pytest.mark.parametrize("Hq,Hkv,n", [(8, 8, 1), (8, 4, 3), (16, 2, 16),
-                                      (4, 1, 32)])
+                                      (4, 1, 32), (8, 8, 48), (16, 8, 40)])
 def test_shapes(Hq, Hkv, n):
     run_verify(2, Hq, Hkv, 300, [100, 7], n, seed=42)
 
