@@ -1,10 +1,10 @@
 // Single-token decode on gfx950: split-K over the cache, memory-bound.
 //
 // "dryft-flash-infer" agent guide, Where the wins are: per-step overhead and
-// the preallocated, strided cache.  A workgroup of eight waves owns (split,
-// kv head, sequence); the cache rows before the new position are cut into
-// near-equal runs, one per split, and wave w owns the 16-key tiles w, w+8,
-// ... of its run.  Every wave loads the small inputs (the position, the raw q
+// the preallocated, strided cache.  A workgroup of kDecodeWaves (nine) waves
+// owns (split, kv head, sequence); the cache rows before the new position are
+// cut into near-equal runs, one per split, and wave w owns the 16-key tiles
+// w, w+9, ... of its run.  Every wave loads the small inputs (the position, the raw q
 // rows of all heads of the group) and forms q' for all heads itself, so no
 // wave waits for another before its first tile; its cache loads (K straight
 // into the A-operand layout of the 16x16x32 bf16 MFMA, V as whole rows) run
@@ -14,7 +14,7 @@
 // of the K operand are permuted to make it so), and O^T = V^T P^T takes V
 // from the rows as loaded, so a tile costs a few dozen vector instructions
 // and no LDS traffic.  Each wave keeps an online softmax per head (running
-// max and sum, the output rescaled when the max grows); the eight waves'
+// max and sum, the output rescaled when the max grows); the waves'
 // (max, sum, output) are combined once, after one barrier.  The new token is
 // folded into split 0: its last wave runs the fp64 K prologue (one RNE) and
 // writes the slot before issuing its own cache loads, and adds the new key to
