@@ -784,7 +784,7 @@ def main():
         "prefill_TFLOPs": round(pre_tflops, 1),
         "prefill_frac_mfma_peak": round(pre_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "verify_us": round(ver_us, 2),
-        "roofline": {"kernel": "qa_decode call = decode_kernel<4,3,true> "
+        "roofline": {"kernel": "qa_decode call = decode_kernel<4,2,true> "
                                "(one launch, merge inside)", "bound": "hbm",
                      "achieved": round(dec_ach, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s",
